@@ -1,0 +1,271 @@
+"""Plain fp64 CPU oracle for the AWQ hot path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The HIP
+library never uses it, and it shares no code, tables or constants with the HIP
+path; it imports nothing from the product package.
+
+Everything here is float64 numpy, written to be checked against the pages by eye:
+no blocking, no fusion, no reordering beyond what each definition states.  A
+library matmul (BLAS dgemm) is used as a step where the definition is a matrix
+product.
+
+Sources (page title -- section):
+
+* [P1] "AWQ (Activation-aware Weight Quantization)" (compassingai.com concept
+  page) -- sections 量化数学基础 (per-group quantizer), AWQ 的缩放如何改变量化误差
+  (error analysis), 重要通道识别的统计依据 (per-channel statistic),
+  缩放因子优化的完整流程 (steps 1-6 of the search), 推理时的等效实现 (offline
+  quantization and the online W4A16 product).
+* [P2] "大模型 AWQ 量化实战：激活感知权重量化（Activation-aware Weight
+  Quantization）部署" (CSDN) -- section 2, the ``quant_config`` with
+  ``zero_point``, ``q_group_size`` and ``w_bit``.
+* [P3] "AWQ 激活感知量化" (aiqz.cc) -- section 1 (importance E|X_i|), section 4
+  (symmetric quantizer, worked values), section 5 (relative error epsilon),
+  section 6 (memory model M = N*b/8, R = 16/b).
+* [P4] "009. AWQ Integration" (blog.yoooo.fun) -- 关键设计 3: the search scores
+  exactly the quantizer that packing uses; Consequences: 4-bit packing, two
+  weights per byte.
+* [P5] "量化推理算法 GPTQ / AWQ" (slowleelab) -- 4.3 AWQ search loop (keep the
+  best loss with a strict "<", so the first minimum wins).
+
+Readings where the pages are silent or disagree (each is listed with its reason
+in the design notes of the repository):
+
+* statistic is mean |x| over all calibration tokens; stored as float32;
+* scale family s_k(alpha) = max(m_k, 1e-8)**alpha, unnormalised, alpha_i = i/20,
+  evaluated in float64 and rounded once to float32;
+* asymmetric quantizer: the group range is widened to include 0,
+  Delta = fl32((max - min)/15) (Delta := 1 if it is 0), zero = clamp(rne(-min/Delta), 0, 15),
+  code = clamp(rne(p/Delta) + zero, 0, 15);
+* symmetric quantizer: Delta = fl32(max|p|/7) (1 if 0), level = clamp(rne(p/Delta), -7, 7),
+  stored code = level + 8, zero = 8 (so one dequant formula (code - zero)*Delta serves both);
+* rounding is round-half-to-even;
+* loss is the plain sum of squares ||X (What - W)||^2, argmin takes the smallest alpha
+  among equal losses.
+
+No function here is "parity unpinned": each is pinned by tests under
+``tests/test_oracle_*.py`` against worked values, closed forms, invariants and
+brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SCALE_FLOOR = 1e-8   # floor on the statistic before taking powers (degenerate zero channels)
+INT4_LEVELS = 16     # [P3] section 4: INT4 has 16 levels
+
+
+# ----------------------------------------------------------------------------- a1
+def act_stats(X: np.ndarray, sum_abs: np.ndarray | None = None,
+              total_tokens: int | None = None):
+    """Per-input-channel statistic m_k = (1/T) sum_t |x_tk|.
+
+    [P1] 重要通道识别的统计依据 (activation_scale[j] = mean |X_calib[:, j]|) and
+    [P3] section 1 (I_i = E[|X_i|], an average over the calibration samples).
+
+    ``X`` is float64 [T, K] (exact upcast of the bf16 input).  ``sum_abs`` (float64
+    [K]) lets the statistic be accumulated over several calibration batches; then
+    ``total_tokens`` is the token count over all batches.  Returns
+    (sum_abs float64 [K], mean_abs float32 [K]); the float32 mean is the stored
+    statistic that everything downstream consumes.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    s = np.abs(X).sum(axis=0)
+    if sum_abs is not None:
+        s = np.asarray(sum_abs, dtype=np.float64) + s
+    n = X.shape[0] if total_tokens is None else int(total_tokens)
+    return s, (s / n).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- a2
+def alpha_grid(n_grid: int = 21) -> np.ndarray:
+    """alpha_i = i/(n_grid-1): [P1] 缩放因子优化的完整流程 step 3, {0, 0.05, ..., 1.0}."""
+    return np.arange(n_grid, dtype=np.float64) / float(n_grid - 1)
+
+
+def scale_table(mean_abs: np.ndarray, n_grid: int = 21) -> np.ndarray:
+    """s[i, k] = fl32(max(m_k, 1e-8) ** alpha_i) -- [P1] step 3, s_j(alpha) = activation_scale[j]**alpha."""
+    m = np.maximum(np.asarray(mean_abs, dtype=np.float32).astype(np.float64), SCALE_FLOOR)
+    a = alpha_grid(n_grid)
+    return np.power(m[None, :], a[:, None]).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- quantizer
+def quantize_groups(P: np.ndarray, group_size: int, zero_point: bool):
+    """Group-wise INT4 quantization of P (float64 [K, N]) along K, per output column.
+
+    [P1] 量化数学基础 (per-group step, round, clamp), [P3] section 4 (symmetric
+    absmax: Delta = max|w_s| / (2**(b-1) - 1) = max|w_s|/7), [P2] section 2
+    (``zero_point`` selects the min-max form with a zero point).
+
+    Returns (codes int64 [K, N] in 0..15, delta float32 [K/g, N], zero int64 [K/g, N]).
+    The dequantized value of an element is (code - zero) * delta.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    K, N = P.shape
+    g = int(group_size)
+    G = P.reshape(K // g, g, N)
+    if zero_point:
+        mx = np.maximum(G.max(axis=1), 0.0)
+        mn = np.minimum(G.min(axis=1), 0.0)
+        delta = ((mx - mn) / 15.0).astype(np.float32)
+        delta[delta == 0] = 1.0
+        d = delta.astype(np.float64)
+        zero = np.clip(np.rint(-mn / d), 0, 15)
+        codes = np.clip(np.rint(G / d[:, None, :]) + zero[:, None, :], 0, 15)
+    else:
+        amax = np.abs(G).max(axis=1)
+        delta = (amax / 7.0).astype(np.float32)
+        delta[delta == 0] = 1.0
+        d = delta.astype(np.float64)
+        zero = np.full(amax.shape, 8.0)
+        codes = np.clip(np.rint(G / d[:, None, :]), -7, 7) + 8
+    return codes.reshape(K, N).astype(np.int64), delta, zero.astype(np.int64)
+
+
+def pre_round_values(P: np.ndarray, delta: np.ndarray, group_size: int, zero_point: bool):
+    """The values that the quantizer rounds: p/Delta per element and, for the
+    asymmetric form, -min/Delta per group.  Used only to count near-ties."""
+    P = np.asarray(P, dtype=np.float64)
+    K, N = P.shape
+    g = int(group_size)
+    d = np.repeat(delta.astype(np.float64), g, axis=0)
+    t = P / d
+    if zero_point:
+        G = P.reshape(K // g, g, N)
+        mn = np.minimum(G.min(axis=1), 0.0)
+        tz = -mn / delta.astype(np.float64)
+    else:
+        tz = np.zeros(delta.shape)
+    return t, tz
+
+
+def near_tie(t: np.ndarray, rel: float = 1e-5) -> np.ndarray:
+    """True where t lies within rel*max(1,|t|) of a .5 rounding boundary."""
+    f = np.abs(t - np.floor(t) - 0.5)
+    return f <= rel * np.maximum(1.0, np.abs(t))
+
+
+def dequantize(codes: np.ndarray, delta: np.ndarray, zero: np.ndarray, group_size: int) -> np.ndarray:
+    """(code - zero) * Delta, broadcast per group along K -- float64 [K, N]."""
+    g = int(group_size)
+    d = np.repeat(np.asarray(delta, dtype=np.float64), g, axis=0)
+    z = np.repeat(np.asarray(zero, dtype=np.float64), g, axis=0)
+    return (np.asarray(codes, dtype=np.float64) - z) * d
+
+
+def fake_quant(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
+               quantizer=None) -> np.ndarray:
+    """What = S^-1 Q(S W): [P1] step 4a-4b and [P5] 4.3 (What = quant(W diag(s)) diag(s)^-1).
+
+    ``W`` float64 [K, N] (input channel k is row k), ``s`` float32/64 [K].
+    ``quantizer`` (default: the group INT4 quantizer followed by dequantization)
+    maps the scaled weights to their dequantized values; tests substitute the
+    identity to check that scaling alone is exact.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    s64 = np.asarray(s, dtype=np.float64)
+    P = s64[:, None] * W
+    if quantizer is None:
+        codes, delta, zero = quantize_groups(P, group_size, zero_point)
+        Ph = dequantize(codes, delta, zero, group_size)
+    else:
+        Ph = quantizer(P)
+    return Ph / s64[:, None]
+
+
+# ----------------------------------------------------------------------------- a3/a4
+def loss(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
+         quantizer=None) -> float:
+    """L = ||X (S^-1 Q(S W) - W)||^2: [P1] step 4c, with the error analysis of
+    AWQ 的缩放如何改变量化误差 (Delta Y = X S^-1 eps_SW)."""
+    E = fake_quant(W, s, group_size, zero_point, quantizer) - np.asarray(W, dtype=np.float64)
+    Y = np.asarray(X, dtype=np.float64) @ E
+    return float(np.sum(Y * Y))
+
+
+def losses(X: np.ndarray, W: np.ndarray, S: np.ndarray, group_size: int, zero_point: bool,
+           quantizer=None) -> np.ndarray:
+    """L(alpha_i) for every row s_i of the scale table S [n_grid, K]."""
+    return np.array([loss(X, W, S[i], group_size, zero_point, quantizer) for i in range(S.shape[0])])
+
+
+def select(L: np.ndarray) -> int:
+    """alpha* = argmin L, first minimum on ties: [P1] step 5, [P5] 4.3 (strict "<")."""
+    best = 0
+    for i in range(1, len(L)):
+        if L[i] < L[best]:
+            best = i
+    return best
+
+
+def search(X: np.ndarray, W: np.ndarray, mean_abs: np.ndarray, group_size: int,
+           zero_point: bool, n_grid: int = 21):
+    """The whole per-layer search ([P1] steps 3-6).  Returns a dict with the scale
+    table, every loss, the chosen index and s* = s[best]."""
+    S = scale_table(mean_abs, n_grid)
+    L = losses(X, W, S, group_size, zero_point)
+    b = select(L)
+    return {"S": S, "losses": L, "best": b, "s_best": S[b].copy()}
+
+
+def relative_error(L: float, X: np.ndarray, W: np.ndarray) -> float:
+    """epsilon = ||X (W - What)||^2 / ||X W||^2: [P3] section 5."""
+    Y = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+    return float(L / np.sum(Y * Y))
+
+
+# ----------------------------------------------------------------------------- a5
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte ([P4] Consequences): word (i, n) of the uint32
+    [K/8, N] result holds codes[8i + j, n] in bits 4j..4j+3."""
+    codes = np.asarray(codes)
+    K, N = codes.shape
+    c = codes.reshape(K // 8, 8, N).astype(np.uint32)
+    out = np.zeros((K // 8, N), dtype=np.uint32)
+    for j in range(8):
+        out |= (c[:, j, :] & np.uint32(0xF)) << np.uint32(4 * j)
+    return out
+
+
+def unpack_nibbles(words: np.ndarray) -> np.ndarray:
+    words = np.asarray(words, dtype=np.uint32)
+    Kw, N = words.shape
+    out = np.empty((Kw, 8, N), dtype=np.int64)
+    for j in range(8):
+        out[:, j, :] = (words >> np.uint32(4 * j)) & np.uint32(0xF)
+    return out.reshape(Kw * 8, N)
+
+
+def pack(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool):
+    """Offline quantization W_q = Quantize(diag(s*) W) ([P1] 推理时的等效实现),
+    stored as (codes uint32 [K/8, N], scales float32 [K/g, N], zeros uint8 [K/g, N])."""
+    P = np.asarray(s, dtype=np.float64)[:, None] * np.asarray(W, dtype=np.float64)
+    codes, delta, zero = quantize_groups(P, group_size, zero_point)
+    return pack_nibbles(codes), delta.astype(np.float32), zero.astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- a6
+def w4a16_ref(X: np.ndarray, s: np.ndarray, words: np.ndarray, scales: np.ndarray,
+              zeros: np.ndarray, group_size: int) -> np.ndarray:
+    """Y = (X diag(1/s*)) Dequant(W_q) ([P1] 推理时的等效实现, online step) in float64."""
+    Wd = dequantize(unpack_nibbles(words), scales, zeros, group_size)
+    Xs = np.asarray(X, dtype=np.float64) / np.asarray(s, dtype=np.float64)[None, :]
+    return Xs @ Wd
+
+
+# ----------------------------------------------------------------------------- sizes
+def packed_bytes(n_params: float, bits: int) -> float:
+    """M = N*b/8 bytes ([P3] section 6)."""
+    return n_params * bits / 8.0
+
+
+def compression_ratio(bits: int) -> float:
+    """R = 16/b relative to 16-bit weights ([P3] section 6)."""
+    return 16.0 / bits
+
+
+def storage_bytes(K: int, N: int, group_size: int) -> dict:
+    """Bytes of the stored layer: nibble codes plus float32 scales and uint8 zeros."""
+    return {"codes": K * N // 2, "scales": 4 * (K // group_size) * N, "zeros": (K // group_size) * N}
