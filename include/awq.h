@@ -1,0 +1,156 @@
+/*
+ * awq.h -- C ABI of libawq, the MI355X (gfx950) implementation of the AWQ
+ * (activation-aware weight quantization) hot path.
+ *
+ * The library computes, for one linear layer Y = X W with W laid out
+ * [K = input channels, N = output channels]:
+ *   1. the per-input-channel activation statistic m_k = mean_t |x_tk|;
+ *   2. the per-layer scale search over alpha_i = i/(n_grid-1), scoring
+ *      L(alpha) = || X (S^-1 Q(S W) - W) ||^2 with S = diag(m^alpha);
+ *   3. INT4 packing of the winning S* W (codes, per-group scales and zeros) and
+ *      the W4A16 product Y = (X / s*) Dequant(Wq).
+ *
+ * Sources (page title -- section), for the definitions cited below:
+ *   [P1] "AWQ (Activation-aware Weight Quantization)" (compassingai.com)
+ *   [P2] "大模型 AWQ 量化实战：激活感知权重量化（Activation-aware Weight Quantization）部署" (CSDN)
+ *   [P3] "AWQ 激活感知量化" (aiqz.cc)
+ *   [P4] "009. AWQ Integration" (blog.yoooo.fun)
+ *   [P5] "量化推理算法 GPTQ / AWQ" (slowleelab)
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronizes; scratch space is the caller's `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *     enqueued asynchronously; outputs are valid once the stream has completed it.
+ *   - Matrices are row-major and contiguous.  bf16 inputs and all outputs must be
+ *     16-byte aligned.
+ *   - Argument errors are detected on the host BEFORE anything is enqueued; then the
+ *     call returns a negative status and writes nothing.  AWQ_ERR_HIP is returned when
+ *     a kernel launch fails (outputs are then unspecified).
+ *   - Calls on distinct streams with distinct outputs and workspaces may run
+ *     concurrently.  Calls that share a workspace must be ordered by the caller.
+ *   - Results are deterministic: no floating-point atomics; every reduction has a
+ *     fixed order, so repeated calls on the same inputs give bit-identical outputs.
+ */
+#ifndef AWQ_H_
+#define AWQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AWQ_OK 0
+#define AWQ_ERR_INVALID_ARG (-1) /* null/misaligned pointer, non-positive size, K % group_size != 0, ... */
+#define AWQ_ERR_UNSUPPORTED (-2) /* w_bit != 4, group_size not in {32, 64, 128}, n_grid outside [2, 64] */
+#define AWQ_ERR_WORKSPACE (-3)   /* workspace smaller than the matching *_workspace_size() */
+#define AWQ_ERR_HIP (-4)         /* a HIP call failed; awq_last_hip_error() holds its code */
+
+/* Quantization settings ([P4] 架构, AWQConfig; [P2] section 2, quant_config).
+ *   w_bit       bits per weight; only 4 is supported.
+ *   group_size  g: consecutive input channels (rows of W) sharing one step and zero,
+ *               per output column.  Supported: 32, 64, 128.
+ *   zero_point  1 = asymmetric min-max with a zero point: Delta = (max - min)/15 over the
+ *               group range widened to include 0, zero = clamp(rne(-min/Delta), 0, 15),
+ *               code = clamp(rne(p/Delta) + zero, 0, 15).
+ *               0 = symmetric absmax ([P3] section 4; [P1] 量化数学基础): Delta = max|p|/7,
+ *               level = clamp(rne(p/Delta), -7, 7), stored code = level + 8, zero = 8.
+ *               In both modes Delta := 1 when the group is all zero, and the dequantized
+ *               value is (code - zero) * Delta.
+ *   n_grid      number of alpha points, alpha_i = i/(n_grid-1) ([P1] 缩放因子优化的完整流程
+ *               step 3 uses 21: {0, 0.05, ..., 1}).  Supported: 2..64.
+ */
+typedef struct awq_qconfig {
+    int32_t w_bit;
+    int32_t group_size;
+    int32_t zero_point;
+    int32_t n_grid;
+} awq_qconfig;
+
+/* ---------------------------------------------------------------- a1: statistic
+ * Per-input-channel mean absolute activation ([P1] 重要通道识别的统计依据;
+ * [P3] section 1, I_i = E|X_i|; [P4] AWQQuantizer.add_batch accumulates it over
+ * calibration batches).
+ *   X          bf16 [T, K] calibration activations (T tokens).
+ *   sum_abs    float64 [K], in/out.  accumulate = 0: overwritten with sum_t |x_tk|;
+ *              accumulate = 1: the batch's sums are added to the values it holds.
+ *   total_tokens  token count of all batches accumulated so far (>= T); the mean is
+ *              sum_abs / total_tokens.
+ *   mean_abs   float32 [K] out (may be NULL): the float32 rounding of that mean.
+ *   workspace  >= awq_act_stats_workspace_size(T, K) bytes (fixed-order partial sums).
+ * The float64 sums are exact whenever each channel's values span less than about
+ * 2^30 in magnitude, so the result does not depend on summation order.
+ */
+size_t awq_act_stats_workspace_size(int64_t T, int64_t K);
+int awq_act_stats(const void* X_bf16, int64_t T, int64_t K, double* sum_abs, int accumulate,
+                  int64_t total_tokens, float* mean_abs, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------- a2: scale table
+ * s[i, k] = float32( max(m_k, 1e-8) ^ alpha_i ), alpha_i = i/(n_grid-1), evaluated in
+ * float64 ([P1] 缩放因子优化的完整流程 step 3: s_j(alpha) = activation_scale[j]^alpha).
+ *   mean_abs   float32 [K];  s_table  float32 [n_grid, K] out.
+ */
+int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_table, void* stream);
+
+/* ---------------------------------------------------------------- a3 + a4: search
+ * For every alpha_i: group-quantize diag(s_i) W, dequantize, divide by s_i, and score
+ *   L_i = || X (S_i^-1 Q(S_i W) - W) ||^2
+ * ([P1] 缩放因子优化的完整流程 steps 4a-4c; [P5] 4.3 search loop), then pick the first
+ * minimum ([P1] step 5; [P5] 4.3 keeps a loss only if strictly smaller) and record
+ * s* = s_best ([P1] step 6).
+ *   X        bf16 [T, K];  W  bf16 [K, N];  mean_abs  float32 [K] (from awq_act_stats).
+ *   losses   float64 [n_grid] out;  best  int32 [1] out;  s_best  float32 [K] out.
+ *   workspace >= awq_search_workspace_size(T, K, N, cfg) bytes.
+ * One fused kernel per (token tile, column tile, alpha slice): the tile of X is loaded
+ * once and reused for every alpha of the slice, each E_i tile is quantized and
+ * dequantized in registers, X E_i runs on bf16 matrix cores with float32 accumulation,
+ * and only sum-of-squares partials leave the kernel.  Losses are exact sums of those
+ * float32 products; they agree with a float64 evaluation to about 1e-3 relative.
+ */
+size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg);
+int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N,
+               const float* mean_abs, const awq_qconfig* cfg, void* workspace, size_t ws_bytes,
+               double* losses, int32_t* best, float* s_best, void* stream);
+
+/* ---------------------------------------------------------------- a5: pack
+ * Offline quantization W_q = Quantize(diag(s) W) ([P1] 推理时的等效实现, 预处理), with
+ * the quantizer of awq_qconfig evaluated in float64 (p = s*w is exact there), stored as
+ *   codes   uint32 [K/8, N]: bits 4j..4j+3 of word (i, n) hold the code of row 8i+j
+ *           (two 4-bit weights per byte, [P4] Consequences; [P3] section 6, M = N*b/8);
+ *   scales  float32 [K/g, N]: Delta per (group, column);
+ *   zeros   uint8   [K/g, N]: zero per (group, column) (8 in symmetric mode).
+ *   W  bf16 [K, N];  s  float32 [K] (normally s_best from awq_search).
+ */
+int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg,
+             uint32_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/* ---------------------------------------------------------------- a6: W4A16 product
+ * Y[m, n] = sum_k (x_mk / s_k) * (code_kn - zero_gn) * Delta_gn,  g = k / group_size
+ * ([P1] 推理时的等效实现, 推理: Y = (X diag(1/s*)) Dequant(W_q), with the 1/s* scaling
+ * folded into the kernel as the page suggests; [P2] section 3, 4-bit weights unpacked
+ * on chip and multiplied with 16-bit activations).
+ *   X  bf16 [M, K];  s  float32 [K];  codes/scales/zeros as written by awq_pack;
+ *   Y  bf16 [M, N] out.  Accumulation is float32; x/s is rounded to bf16 once.
+ *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes.  It holds
+ *   split-K partials and arrival counters: it must be zero-filled before its first use,
+ *   and every completed call leaves the counters at zero again.
+ * Requires N % 8 == 0.
+ */
+size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size);
+int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes,
+                   const float* scales, const uint8_t* zeros, int64_t K, int64_t N,
+                   int32_t group_size, void* Y_bf16, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* ---------------------------------------------------------------- status helpers */
+const char* awq_status_string(int status);
+int awq_last_hip_error(void);   /* hipError_t of the most recent AWQ_ERR_HIP on this thread */
+const char* awq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_H_ */

@@ -1,0 +1,163 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the same seeded inputs.
+
+Bars:
+  * statistic and scale table: bit-exact (float64 sums are exact on these inputs; the scale
+    table is one float64 pow rounded to float32 on both sides);
+  * pack: codes, steps and zeros bit-exact given the same s (both sides evaluate the
+    quantizer in float64); elements whose pre-round value is within 1e-5 relative of a .5
+    boundary would be exempt and are counted;
+  * search: every L(alpha) within 1e-2 relative of the oracle; the chosen alpha's oracle loss
+    within 1e-2 of the oracle minimum; s_best equal to the oracle's scale row of that alpha;
+  * W4A16 product: relative Frobenius error <= 2e-2 against the fp64 reference.
+Shapes span several tiles with ragged tails in T (token tiles of 512 rows) and N (column
+tiles of 16), both quantizer modes, all supported group sizes and non-default grids.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import awq_oracle as O
+from weight_only_int4_act_amd import inputs as I
+from tests.gpu_util import awq, gpu_gemm, gpu_layer, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+L_TOL = 1e-2
+GEMM_TOL = 2e-2
+
+CASES = {
+    # name: (T, K, N, group_size, zero_point, n_grid, seed)
+    "c1": None,
+    "ragged": (300, 384, 40, 128, True, 21, 1),
+    "sym64": (1030, 256, 48, 64, False, 21, 2),
+    "g32_grid11": (100, 192, 24, 32, True, 11, 3),
+    "grid2_minK": (64, 128, 16, 128, True, 2, 4),
+    "sym128_multi": (700, 512, 72, 128, False, 21, 5),
+}
+
+_cache = {}
+
+
+def _case(name):
+    if name in _cache:
+        return _cache[name]
+    if name == "c1":
+        L = I.make_config("c1").layers[0]
+        g, zp, ng = 128, True, 21
+    else:
+        T, K, N, g, zp, ng, seed = CASES[name]
+        L = I.small(T, K, N, seed=seed, group_size=g, zero_point=zp)
+    log(f"[parity] case {name}: T={L.X.shape[0]} K={L.X.shape[1]} N={L.W.shape[1]} g={g} zp={zp} n_grid={ng}")
+    X64, W64 = I.bf16_to_f64(L.X), I.bf16_to_f64(L.W)
+    gpu = gpu_layer(L.X, L.W, g, zp, ng)
+    s, m = O.act_stats(X64)
+    S = O.scale_table(m, ng)
+    Lo = O.losses(X64, W64, S, g, zp)
+    _cache[name] = (L, X64, W64, g, zp, ng, gpu, s, m, S, Lo)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_stats_and_scale_table_bit_exact(name):
+    L, X64, W64, g, zp, ng, gpu, s, m, S, Lo = _case(name)
+    assert np.array_equal(gpu["sum_abs"], s), f"sum_abs mismatches: {(gpu['sum_abs'] != s).sum()}"
+    assert np.array_equal(gpu["mean_abs"], m), f"mean_abs mismatches: {(gpu['mean_abs'] != m).sum()}"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_search_losses_and_choice(name):
+    L, X64, W64, g, zp, ng, gpu, s, m, S, Lo = _case(name)
+    Lg = gpu["losses"]
+    rel = np.abs(Lg - Lo) / np.maximum(Lo, 1e-300)
+    log(f"[parity] {name}: max rel L err {rel.max():.3e}, best gpu {gpu['best']} oracle {O.select(Lo)}")
+    assert np.all(rel <= L_TOL), rel
+    b = gpu["best"]
+    assert 0 <= b < ng
+    assert Lo[b] <= (1 + L_TOL) * Lo.min()
+    assert np.array_equal(gpu["s_best"], S[b])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_pack_bit_exact(name):
+    L, X64, W64, g, zp, ng, gpu, s, m, S, Lo = _case(name)
+    b = gpu["best"]
+    w, d, z = O.pack(W64, S[b], g, zp)
+    P = S[b].astype(np.float64)[:, None] * W64
+    t, tz = O.pre_round_values(P, d, g, zp)
+    ties = O.near_tie(t) | np.repeat(O.near_tie(tz), g, axis=0)
+    codes_o = O.unpack_nibbles(w)
+    codes_g = O.unpack_nibbles(gpu["codes"])
+    bad = codes_o != codes_g
+    log(f"[parity] {name}: pack code mismatches {bad.sum()} (near-ties {ties.sum()})")
+    assert not np.any(bad & ~ties)
+    assert np.array_equal(gpu["scales"], d)
+    assert np.array_equal(gpu["zeros"], z)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_gemm_and_closure(name):
+    L, X64, W64, g, zp, ng, gpu, s, m, S, Lo = _case(name)
+    q = gpu["q"]
+    T = X64.shape[0]
+    for M in sorted({1, 7, 16, 37, min(T, 256), T}):
+        Y = gpu_gemm(L.X[:M].contiguous(), q)
+        Yr = O.w4a16_ref(X64[:M], gpu["s_best"], gpu["codes"], gpu["scales"], gpu["zeros"], g)
+        err = rel_fro(Y, Yr)
+        assert err <= GEMM_TOL, (M, err)
+    # closure: the packed layer's output error on the calibration set is the search's L(alpha*)
+    Y = gpu_gemm(L.X, q)
+    Lc = float(np.sum((Y - X64 @ W64) ** 2))
+    Lb = gpu["losses"][gpu["best"]]
+    log(f"[parity] {name}: closure L {Lc:.6e} vs search {Lb:.6e}")
+    assert abs(Lc - Lb) <= 2e-2 * Lb
+
+
+def test_deterministic_reruns():
+    Lr = I.small(600, 256, 32, seed=9)
+    a = gpu_layer(Lr.X, Lr.W, 128, True)
+    b = gpu_layer(Lr.X, Lr.W, 128, True)
+    for k in ("sum_abs", "mean_abs", "losses", "s_best", "codes", "scales", "zeros"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["best"] == b["best"]
+    y1 = gpu_gemm(Lr.X[:16].contiguous(), a["q"])
+    y2 = gpu_gemm(Lr.X[:16].contiguous(), a["q"])
+    assert np.array_equal(y1, y2)
+
+
+def test_degenerate_inputs():
+    # all-zero activations: every loss is 0, the first alpha wins, s* = 1 (alpha = 0 row)
+    T, K, N = 40, 128, 16
+    X = torch.zeros((T, K), dtype=torch.bfloat16)
+    W = I.small(T, K, N, seed=11).W
+    r = gpu_layer(X, W, 128, True)
+    assert np.all(r["losses"] == 0.0) and r["best"] == 0 and np.all(r["s_best"] == 1.0)
+    assert np.all(r["mean_abs"] == 0.0)
+    # all-zero weights: zero error for every alpha; steps are 1 and codes are 0
+    L = I.small(T, K, N, seed=12)
+    r = gpu_layer(L.X, torch.zeros((K, N), dtype=torch.bfloat16), 128, True)
+    assert np.all(r["losses"] == 0.0) and r["best"] == 0
+    assert np.all(r["scales"] == 1.0) and np.all(r["codes"] == 0) and np.all(r["zeros"] == 0)
+
+
+def test_stats_accumulate_and_unaligned_k():
+    A = awq()
+    Lr = I.small(333, 390, 8, seed=13)        # K % 8 != 0 takes the scalar path
+    X = Lr.X.cuda()
+    T, K = X.shape
+    ws = A.workspace(A.awq_act_stats_workspace_size(T, K), X.device)
+    s = torch.empty(K, dtype=torch.float64, device="cuda")
+    m = torch.empty(K, dtype=torch.float32, device="cuda")
+    A.awq_act_stats(X[:200].contiguous(), s, False, 200, None, ws)
+    A.awq_act_stats(X[200:].contiguous(), s, True, T, m, ws)
+    torch.cuda.synchronize()
+    so, mo = O.act_stats(I.bf16_to_f64(Lr.X))
+    assert np.array_equal(s.cpu().numpy(), so) and np.array_equal(m.cpu().numpy(), mo)
+
+
+def test_scale_table_entry_point():
+    A = awq()
+    m = np.array([0.0, 1e-9, 0.25, 1.0, 4.0, 100.0, 3.7, 1e30], dtype=np.float32)
+    out = torch.empty((21, m.size), dtype=torch.float32, device="cuda")
+    A.awq_scale_table(torch.from_numpy(m).cuda(), 21, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), O.scale_table(m, 21))

@@ -1,0 +1,99 @@
+"""Host-side checks of libawq that need no GPU: the shared library loads, exports every
+function include/awq.h declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+LIB = os.path.join(ROOT, "weight_only_int4_act_amd", "libawq.so")
+
+
+def _declared():
+    txt = open(HEADER, encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"\b(awq_\w+)\s*\(", txt)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not os.path.exists(LIB):
+        pytest.fail("libawq.so is not built (python -m weight_only_int4_act_amd.build)")
+    from weight_only_int4_act_amd import awq as mod
+    return mod
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("awq_act_stats", "awq_search", "awq_pack", "awq_w4a16_gemm", "awq_scale_table",
+               "awq_search_workspace_size", "awq_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(awq):
+    lib = awq.library()
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} is declared in awq.h but not exported"
+    assert set(_declared()) == set(awq.EXPORTED)
+
+
+def test_status_strings(awq):
+    assert awq.awq_status_string(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert awq.awq_status_string(st) not in ("ok", "unknown status")
+    assert awq.awq_status_string(7) == "unknown status"
+    assert "gfx950" in awq.awq_version()
+
+
+def test_workspace_sizes(awq):
+    cfg = awq.qconfig(128, True, 21)
+    assert awq.awq_search_workspace_size(8192, 4096, 4096, cfg) > 0
+    assert awq.awq_search_workspace_size(8192, 4100, 4096, cfg) == 0          # K % g != 0
+    assert awq.awq_search_workspace_size(8192, 4096, 4096, awq.qconfig(48, True, 21)) == 0
+    assert awq.awq_act_stats_workspace_size(8192, 4096) >= 8 * 4096
+    assert awq.awq_act_stats_workspace_size(0, 4096) == 0
+
+
+def test_host_validation_rejects_before_launch(awq):
+    lib = awq.library()
+    p = ctypes.c_void_p(256)          # never dereferenced: every call below fails validation first
+    nul = ctypes.c_void_p(0)
+    cfg = awq.qconfig(128, True, 21)
+    ws = ctypes.c_size_t(1 << 40)
+    # search: null pointers, bad shapes, unsupported configurations, misalignment
+    assert lib.awq_search(nul, 8, p, 128, 16, p, ctypes.byref(cfg), p, ws, p, p, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search(p, 0, p, 128, 16, p, ctypes.byref(cfg), p, ws, p, p, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search(p, 8, p, 100, 16, p, ctypes.byref(cfg), p, ws, p, p, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    for bad in (awq.qconfig(128, True, 21, w_bit=3), awq.qconfig(96, True, 21), awq.qconfig(128, True, 1),
+                awq.qconfig(128, True, 65)):
+        assert lib.awq_search(p, 8, p, 128, 16, p, ctypes.byref(bad), p, ws, p, p, p, nul) == awq.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_search(ctypes.c_void_p(258), 8, p, 128, 16, p, ctypes.byref(cfg), p, ws, p, p, p,
+                          nul) == awq.AWQ_ERR_INVALID_ARG
+    need = awq.awq_search_workspace_size(8, 128, 16, cfg)
+    assert lib.awq_search(p, 8, p, 128, 16, p, ctypes.byref(cfg), p, need - 1, p, p, p,
+                          nul) == awq.AWQ_ERR_WORKSPACE
+    # stats
+    assert lib.awq_act_stats(p, 8, 16, nul, 0, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_act_stats(p, 8, 16, p, 0, 7, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG   # total < T
+    assert lib.awq_act_stats(p, 8, 16, p, 2, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_act_stats(p, 4096, 4096, p, 0, 4096, p, p, 8, nul) == awq.AWQ_ERR_WORKSPACE
+    # scale table
+    assert lib.awq_scale_table(p, 16, 1, p, nul) == awq.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_scale_table(nul, 16, 21, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    # pack
+    assert lib.awq_pack(p, 100, 16, p, ctypes.byref(cfg), p, p, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_pack(p, 128, 16, p, ctypes.byref(awq.awq_qconfig(4, 128, 2, 21)), p, p, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    # gemm
+    assert lib.awq_w4a16_gemm(p, 1, p, p, p, p, 128, 12, 128, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG  # N % 8
+    assert lib.awq_w4a16_gemm(p, 1, p, p, p, p, 128, 16, 256, p, p, ws, nul) == awq.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_w4a16_gemm(p, 0, p, p, p, p, 128, 16, 128, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors(awq):
+    import torch
+    X = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        awq.awq_act_stats(X, torch.zeros(128, dtype=torch.float64), False, 4, None, torch.zeros(8, dtype=torch.uint8))

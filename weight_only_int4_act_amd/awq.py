@@ -1,0 +1,214 @@
+"""Thin Python binding of libawq (include/awq.h).
+
+Argument marshalling only: every function passes device pointers of torch tensors, sizes and
+the current HIP stream to the C entry point of the same name, and raises ``AwqError`` on a
+non-zero status.  torch is used for device memory and streams; every step of the path runs
+in the library's HIP kernels.  If ``libawq.so`` has not been built the import of this module
+fails loudly -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libawq.so")
+
+AWQ_OK = 0
+AWQ_ERR_INVALID_ARG = -1
+AWQ_ERR_UNSUPPORTED = -2
+AWQ_ERR_WORKSPACE = -3
+AWQ_ERR_HIP = -4
+
+
+class AwqError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip: int = 0):
+        super().__init__(f"{fn} failed with status {status}: {msg}" + (f" (hipError {hip})" if hip else ""))
+        self.status = status
+        self.hip_error = hip
+
+
+class awq_qconfig(ctypes.Structure):
+    _fields_ = [("w_bit", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("zero_point", ctypes.c_int32), ("n_grid", ctypes.c_int32)]
+
+
+def qconfig(group_size: int = 128, zero_point: bool = True, n_grid: int = 21, w_bit: int = 4) -> awq_qconfig:
+    return awq_qconfig(int(w_bit), int(group_size), 1 if zero_point else 0, int(n_grid))
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_CFG = ctypes.POINTER(awq_qconfig)
+
+_SIGNATURES = {
+    "awq_act_stats_workspace_size": (_SZ, [_I64, _I64]),
+    "awq_act_stats": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _I64, _P, _P, _SZ, _P]),
+    "awq_scale_table": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "awq_search_workspace_size": (_SZ, [_I64, _I64, _I64, _CFG]),
+    "awq_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
+    "awq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _CFG, _P, _P, _P, _P]),
+    "awq_w4a16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "awq_w4a16_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
+    "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "awq_last_hip_error": (ctypes.c_int, []),
+    "awq_version": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m weight_only_int4_act_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libawq takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libawq takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != AWQ_OK:
+        msg = _lib.awq_status_string(status).decode()
+        raise AwqError(fn, status, msg, _lib.awq_last_hip_error() if status == AWQ_ERR_HIP else 0)
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """Zero-filled device scratch of at least ``nbytes`` bytes (256-byte aligned by torch)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+def awq_act_stats_workspace_size(T: int, K: int) -> int:
+    return int(_lib.awq_act_stats_workspace_size(T, K))
+
+
+def awq_act_stats(X: torch.Tensor, sum_abs: torch.Tensor, accumulate: bool, total_tokens: int,
+                  mean_abs: Optional[torch.Tensor], ws: torch.Tensor, stream=None) -> None:
+    T, K = X.shape
+    _check("awq_act_stats", _lib.awq_act_stats(_ptr(X), T, K, _ptr(sum_abs), 1 if accumulate else 0,
+                                               int(total_tokens), _ptr(mean_abs), _ptr(ws), _nbytes(ws),
+                                               _stream(stream)))
+
+
+def awq_scale_table(mean_abs: torch.Tensor, n_grid: int, s_table: torch.Tensor, stream=None) -> None:
+    _check("awq_scale_table", _lib.awq_scale_table(_ptr(mean_abs), mean_abs.numel(), int(n_grid),
+                                                   _ptr(s_table), _stream(stream)))
+
+
+def awq_search_workspace_size(T: int, K: int, N: int, cfg: awq_qconfig) -> int:
+    return int(_lib.awq_search_workspace_size(T, K, N, ctypes.byref(cfg)))
+
+
+def awq_search(X: torch.Tensor, W: torch.Tensor, mean_abs: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
+               losses: torch.Tensor, best: torch.Tensor, s_best: torch.Tensor, stream=None) -> None:
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [T, {K}] but W is [{K2}, N]")
+    _check("awq_search", _lib.awq_search(_ptr(X), T, _ptr(W), K, N, _ptr(mean_abs), ctypes.byref(cfg), _ptr(ws),
+                                         _nbytes(ws), _ptr(losses), _ptr(best), _ptr(s_best), _stream(stream)))
+
+
+def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, codes: torch.Tensor, scales: torch.Tensor,
+             zeros: torch.Tensor, stream=None) -> None:
+    K, N = W.shape
+    _check("awq_pack", _lib.awq_pack(_ptr(W), K, N, _ptr(s), ctypes.byref(cfg), _ptr(codes), _ptr(scales),
+                                     _ptr(zeros), _stream(stream)))
+
+
+def awq_w4a16_gemm_workspace_size(M: int, K: int, N: int, group_size: int) -> int:
+    return int(_lib.awq_w4a16_gemm_workspace_size(M, K, N, group_size))
+
+
+def awq_w4a16_gemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                   zeros: torch.Tensor, group_size: int, Y: torch.Tensor, ws: Optional[torch.Tensor],
+                   stream=None) -> None:
+    M, K = X.shape
+    N = codes.shape[1]
+    _check("awq_w4a16_gemm", _lib.awq_w4a16_gemm(_ptr(X), M, _ptr(s), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                                 K, N, int(group_size), _ptr(Y), _ptr(ws), _nbytes(ws),
+                                                 _stream(stream)))
+
+
+def awq_status_string(status: int) -> str:
+    return _lib.awq_status_string(status).decode()
+
+
+def awq_version() -> str:
+    return _lib.awq_version().decode()
+
+
+# ------------------------------------------------------------------ allocation helpers (plumbing only)
+class Quantized:
+    """Device buffers of one packed layer: codes uint32 [K/8, N] (stored as int32), scales float32
+    [K/g, N], zeros uint8 [K/g, N], the input scales s* [K] and the group size."""
+
+    def __init__(self, codes, scales, zeros, s, group_size):
+        self.codes, self.scales, self.zeros, self.s, self.group_size = codes, scales, zeros, s, group_size
+
+
+def run_layer(X: torch.Tensor, W: torch.Tensor, cfg: awq_qconfig, stream=None) -> dict:
+    """Allocate outputs and run stats -> search -> pack for one layer on the current device."""
+    dev = X.device
+    T, K = X.shape
+    N = W.shape[1]
+    sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+    mean_abs = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_stats = workspace(awq_act_stats_workspace_size(T, K), dev)
+    awq_act_stats(X, sum_abs, False, T, mean_abs, ws_stats, stream)
+    ws = workspace(awq_search_workspace_size(T, K, N, cfg), dev)
+    losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    awq_search(X, W, mean_abs, cfg, ws, losses, best, s_best, stream)
+    g = cfg.group_size
+    codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+    zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+    awq_pack(W, s_best, cfg, codes, scales, zeros, stream)
+    return {"sum_abs": sum_abs, "mean_abs": mean_abs, "losses": losses, "best": best,
+            "q": Quantized(codes, scales, zeros, s_best, g)}
+
+
+def gemm(X: torch.Tensor, q: Quantized, stream=None) -> torch.Tensor:
+    M, K = X.shape
+    N = q.codes.shape[1]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    ws = workspace(awq_w4a16_gemm_workspace_size(M, K, N, q.group_size), X.device)
+    awq_w4a16_gemm(X, q.s, q.codes, q.scales, q.zeros, q.group_size, Y, ws, stream)
+    return Y

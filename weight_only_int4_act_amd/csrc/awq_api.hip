@@ -1,0 +1,130 @@
+// C ABI of libawq (declared in include/awq.h): argument validation on the host, then launches on
+// the caller's stream.  Nothing is allocated, freed or synchronized here.
+#include "../../include/awq.h"
+#include "awq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return AWQ_OK;
+    g_last_hip_error = (int)e;
+    return AWQ_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+constexpr int64_t kIntMax = 0x7fffffff;
+
+int check_cfg(const awq_qconfig* cfg, int64_t K) {
+    if (!cfg) return AWQ_ERR_INVALID_ARG;
+    if (cfg->w_bit != 4) return AWQ_ERR_UNSUPPORTED;
+    if (!group_ok(cfg->group_size)) return AWQ_ERR_UNSUPPORTED;
+    if (cfg->n_grid < 2 || cfg->n_grid > 64) return AWQ_ERR_UNSUPPORTED;
+    if (cfg->zero_point != 0 && cfg->zero_point != 1) return AWQ_ERR_INVALID_ARG;
+    if (K % cfg->group_size != 0) return AWQ_ERR_INVALID_ARG;
+    return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t awq_act_stats_workspace_size(int64_t T, int64_t K) {
+    if (T <= 0 || K <= 0) return 0;
+    return awq::plan_stats(T, K).ws_bytes;
+}
+
+int awq_act_stats(const void* X_bf16, int64_t T, int64_t K, double* sum_abs, int accumulate,
+                  int64_t total_tokens, float* mean_abs, void* workspace, size_t ws_bytes, void* stream) {
+    if (!X_bf16 || !sum_abs || T <= 0 || K <= 0 || total_tokens < T) return AWQ_ERR_INVALID_ARG;
+    if (accumulate != 0 && accumulate != 1) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(X_bf16, 16) || !aligned(sum_abs, 8) || (mean_abs && !aligned(mean_abs, 4)))
+        return AWQ_ERR_INVALID_ARG;
+    const awq::StatsPlan p = awq::plan_stats(T, K);
+    if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_stats((const uint16_t*)X_bf16, T, K, sum_abs, accumulate, total_tokens,
+                                        mean_abs, (double*)workspace, p, (hipStream_t)stream));
+}
+
+int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_table, void* stream) {
+    if (!mean_abs || !s_table || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (n_grid < 2 || n_grid > 64) return AWQ_ERR_UNSUPPORTED;
+    if (!aligned(mean_abs, 4) || !aligned(s_table, 4)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_scale_table(mean_abs, K, n_grid, s_table, nullptr, (hipStream_t)stream));
+}
+
+size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg) {
+    if (T <= 0 || K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
+    return awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid).ws_bytes;
+}
+
+int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* mean_abs,
+               const awq_qconfig* cfg, void* workspace, size_t ws_bytes, double* losses, int32_t* best,
+               float* s_best, void* stream) {
+    if (!X_bf16 || !W_bf16 || !mean_abs || !losses || !best || !s_best) return AWQ_ERR_INVALID_ARG;
+    if (T <= 0 || K <= 0 || N <= 0 || T > kIntMax || K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
+    int st = check_cfg(cfg, K);
+    if (st != AWQ_OK) return st;
+    if (!aligned(X_bf16, 16) || !aligned(W_bf16, 2) || !aligned(mean_abs, 4) || !aligned(losses, 8) ||
+        !aligned(best, 4) || !aligned(s_best, 4))
+        return AWQ_ERR_INVALID_ARG;
+    const awq::SearchPlan p = awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid);
+    if (p.tiles > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (ws_bytes < p.ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs, p,
+                                         workspace, losses, best, s_best, (hipStream_t)stream));
+}
+
+int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg, uint32_t* codes,
+             float* scales, uint8_t* zeros, void* stream) {
+    if (!W_bf16 || !s || !codes || !scales || !zeros || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;
+    int st = check_cfg(cfg, K);
+    if (st != AWQ_OK) return st;
+    if (K / cfg->group_size > 65535) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(W_bf16, 2) || !aligned(s, 4) || !aligned(codes, 4) || !aligned(scales, 4))
+        return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_pack((const uint16_t*)W_bf16, K, N, s, cfg->group_size, cfg->zero_point, codes,
+                                       scales, zeros, (hipStream_t)stream));
+}
+
+size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size) {
+    if (M <= 0 || K <= 0 || N <= 0 || !group_ok(group_size) || K % group_size) return 0;
+    return awq::plan_gemm(M, K, N, group_size).ws_bytes;
+}
+
+int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes, const float* scales,
+                   const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size, void* Y_bf16, void* workspace,
+                   size_t ws_bytes, void* stream) {
+    if (!X_bf16 || !s || !codes || !scales || !zeros || !Y_bf16) return AWQ_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || N <= 0 || N % 8 != 0) return AWQ_ERR_INVALID_ARG;
+    if (!group_ok(group_size)) return AWQ_ERR_UNSUPPORTED;
+    if (K % group_size != 0) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(X_bf16, 16) || !aligned(s, 16) || !aligned(codes, 16) || !aligned(scales, 16) ||
+        !aligned(zeros, 16) || !aligned(Y_bf16, 16))
+        return AWQ_ERR_INVALID_ARG;
+    const awq::GemmPlan p = awq::plan_gemm(M, K, N, group_size);
+    if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_gemm((const uint16_t*)X_bf16, M, s, codes, scales, zeros, K, N, group_size,
+                                       (uint16_t*)Y_bf16, workspace, p, (hipStream_t)stream));
+}
+
+const char* awq_status_string(int status) {
+    switch (status) {
+        case AWQ_OK: return "ok";
+        case AWQ_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or shape)";
+        case AWQ_ERR_UNSUPPORTED: return "unsupported configuration (w_bit, group_size or n_grid)";
+        case AWQ_ERR_WORKSPACE: return "workspace too small";
+        case AWQ_ERR_HIP: return "HIP runtime error (see awq_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int awq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* awq_version(void) { return "libawq 0.1 (gfx950)"; }
+
+}  // extern "C"

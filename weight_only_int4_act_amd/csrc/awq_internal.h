@@ -1,0 +1,59 @@
+// Host-side launchers of the libawq kernels (internal; the public ABI is include/awq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// ---- a1: statistic
+struct StatsPlan {
+    int64_t col_blocks;      // workgroups along K (512 channels each)
+    int64_t chunks;          // workgroups along T
+    int64_t rows_per_chunk;
+    size_t ws_bytes;         // float64 partials [chunks, K]
+};
+StatsPlan plan_stats(int64_t T, int64_t K);
+hipError_t launch_stats(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, int accumulate,
+                        int64_t total_tokens, float* mean_abs, double* partials, const StatsPlan& p,
+                        hipStream_t st);
+
+// ---- a2: scale table (and its reciprocal, used inside the search)
+hipError_t launch_scale_table(const float* mean_abs, int64_t K, int n_grid, float* s_tab, float* inv_tab,
+                              hipStream_t st);
+
+// ---- a3/a4: search
+struct SearchPlan {
+    int group_size, n_grid, zero_point;
+    int variant;             // kernel instantiation (see awq_search.hip)
+    int na;                  // alpha slots per workgroup
+    int bm;                  // token rows per workgroup
+    int n_asplit;            // alpha slices
+    int64_t nb;              // 16-column blocks (N rounded up)
+    int64_t tb;              // token blocks
+    int64_t tiles, tiles_per_xcd, grid;
+    // workspace layout (byte offsets)
+    size_t off_s, off_inv, off_wt, off_part, ws_bytes;
+};
+SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid);
+hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                         const float* mean_abs, const SearchPlan& p, void* ws, double* losses,
+                         int32_t* best, float* s_best, hipStream_t st);
+
+// ---- a5: pack
+hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, int group_size,
+                       int zero_point, uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st);
+
+// ---- a6: W4A16 product
+struct GemmPlan {
+    int variant;
+    int64_t grid_x, grid_y, grid_z;
+    int ksplit;
+    size_t off_part, off_cnt, ws_bytes;
+};
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size);
+hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes,
+                       const float* scales, const uint8_t* zeros, int64_t K, int64_t N, int group_size,
+                       uint16_t* Y, void* ws, const GemmPlan& p, hipStream_t st);
+
+}  // namespace awq
