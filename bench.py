@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ hot path on one MI355X.
+
+One step = one pass of the whole path over the 4096x4096 layer with 8192 calibration tokens
+(INT4 asymmetric, g = 128, 21-point alpha grid), inputs resident in HBM:
+    act_stats -> search (scale table, fused loss kernel, loss reduction, argmin) -> pack
+    -> W4A16 product at M = 1, 16 and 256 tokens.
+``value`` is search TFLOP/s over the whole step: 21 * 2*T*K*N flops of X.E products divided
+by the step time (stats, pack and the products included), so it never exceeds the search
+kernels' own rate.
+
+Also reported on the same JSON line:
+  roofline      the search (dominant kernels) against the bf16 matrix-core peak; its duration
+                is measured with HIP events on the stream the library launches on;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the same workload;
+  gemv          the M = 1 W4A16 product over the seven linears of a 70B-shaped block
+                (462 MB of packed weights, rotated so the 256 MB Infinity Cache cannot hold
+                them) against HBM peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "AWQ search TFLOP/s (% bf16 MFMA peak), 4096x4096 layer, 8192 calib tokens"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--gemv-iters", type=int, default=50)
+    ap.add_argument("--cpu-cols", type=int, default=1024,
+                    help="output columns of the oracle's bounded sample (of 4096)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one device copy of known size (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(layer, n_cols):
+    """The fp64 oracle as it stands, on the first n_cols output columns of the same layer:
+    statistic + all 21 losses + argmin.  Returns TFLOP/s of X.E products (same count as value)."""
+    from oracle import awq_oracle as O
+    from weight_only_int4_act_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    X = I.bf16_to_f64(layer.X)
+    W = I.bf16_to_f64(layer.W)[:, :n_cols].copy()
+    T, K = X.shape
+    t0 = time.perf_counter()
+    _, m = O.act_stats(X)
+    res = O.search(X, W, m, layer.group_size, layer.zero_point, 21)
+    dt = time.perf_counter() - t0
+    flops = 21 * 2.0 * T * K * n_cols
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3), "best_alpha_index": int(res["best"]),
+            "sample": f"oracle (numpy float64) statistic + 21-alpha search of the 4096x4096 layer restricted to "
+                      f"its first {n_cols} of 4096 output columns, all 8192 tokens ({flops / 1e12:.3f} TFLOP)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from weight_only_int4_act_amd import awq as A
+    from weight_only_int4_act_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    log("[bench] generating the 4096x4096x8192 layer (seed 0)")
+    layer = I.make_config("c2", seed=0).layers[0]
+    X = layer.X.to(dev)
+    W = layer.W.to(dev)
+    T, K = X.shape
+    N = W.shape[1]
+    g = layer.group_size
+    cfg = A.qconfig(g, layer.zero_point, 21)
+
+    # device buffers (allocated once, outside the timed region)
+    sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+    mean_abs = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_stats = A.workspace(A.awq_act_stats_workspace_size(T, K), dev)
+    ws_search = A.workspace(A.awq_search_workspace_size(T, K, N, cfg), dev)
+    losses = torch.empty(21, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+    zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+    Ms = (1, 16, 256)
+    Xm = {M: X[:M].contiguous() for M in Ms}
+    Ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in Ms}
+    ws_gemm = {M: A.workspace(A.awq_w4a16_gemm_workspace_size(M, K, N, g), dev) for M in Ms}
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        A.awq_act_stats(X, sum_abs, False, T, mean_abs, ws_stats, stream)
+        if i is not None:
+            ev[i][0].record(stream)
+        A.awq_search(X, W, mean_abs, cfg, ws_search, losses, best, s_best, stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        A.awq_pack(W, s_best, cfg, codes, scales, zeros, stream)
+        for M in Ms:
+            A.awq_w4a16_gemm(Xm[M], s_best, codes, scales, zeros, g, Ys[M], ws_gemm[M], stream)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    search_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 21 * 2.0 * T * K * N
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (search_ms * 1e-3) / 1e12
+    log(f"[bench] step {ms_step:.3f} ms, search {search_ms:.3f} ms -> {achieved:.1f} TFLOP/s, best alpha "
+        f"index {int(best.item())}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c2: Llama-7B-shaped 4096x4096 linear, 8192 calibration tokens, INT4 asymmetric "
+                               "g=128, 21-point alpha grid; step = stats + search + pack + W4A16 at M=1,16,256",
+                   "T": T, "K": K, "N": N, "group_size": g, "zero_point": True, "n_grid": 21},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "awq_search call (k_search fused loss kernel + scale table, W tiling, loss "
+                               "reduction and argmin kernels)",
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(search_ms, 4)},
+        "best_alpha_index": int(best.item()),
+    }
+
+    if not args.no_gemv:
+        out["gemv"] = bench_gemv(A, I, torch, dev, args.gemv_iters)
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_cols} columns")
+        out["cpu_baseline"] = cpu_baseline(layer, args.cpu_cols)
+
+    print(json.dumps(out), flush=True)
+
+
+def bench_gemv(A, I, torch, dev, iters):
+    """M = 1 W4A16 product over the seven linears of the 70B-shaped block.  Each layer is run
+    through stats -> search -> pack once (untimed) to produce its packed weights."""
+    layers = []
+    xs = {}
+    log("[bench] gemv: building the 70B-shaped block (7 linears, T=4096)")
+    for l, (name, K, N, j) in enumerate(I.C5_LAYERS):
+        if j not in xs:
+            xs[j] = I.c5_input(0, j).to(dev)
+        Wl = I.c5_weight(0, l).to(dev)
+        r = A.run_layer(xs[j], Wl, A.qconfig(128, True, 21))
+        del Wl
+        q = r["q"]
+        x1 = xs[j][:1].contiguous()
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        ws = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
+        byts = K * N // 2 + 4 * (K // 128) * N + (K // 128) * N + 4 * K + 2 * K + 2 * N
+        layers.append((name, K, N, x1, q, y, ws, byts))
+    xs.clear()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def block():
+        for (name, K, N, x1, q, y, ws, byts) in layers:
+            A.awq_w4a16_gemm(x1, q.s, q.codes, q.scales, q.zeros, 128, y, ws, stream)
+
+    for _ in range(3):
+        block()
+    torch.cuda.synchronize()
+    per = {name: [] for (name, *_r) in layers}
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+           for _ in range(iters)]
+    # block time: back-to-back launches only
+    e0.record(stream)
+    for it in range(iters):
+        block()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1) / iters
+    # per-layer times: events around each launch
+    for it in range(iters):
+        for li, (name, K, N, x1, q, y, ws, byts) in enumerate(layers):
+            evs[it][li][0].record(stream)
+            A.awq_w4a16_gemm(x1, q.s, q.codes, q.scales, q.zeros, 128, y, ws, stream)
+            evs[it][li][1].record(stream)
+    torch.cuda.synchronize()
+    total_bytes = sum(l[-1] for l in layers)
+    res = {"workload": "c5 block M=1: q,k,v,o [8192x8192|1024], gate,up [8192x28672], down [28672x8192], "
+                       "INT4 asym g=128, weights rotated through 7 layers (462 MB) per iteration",
+           "iters": iters, "block_us": round(total_ms * 1e3, 2), "block_bytes": total_bytes,
+           "achieved_GBs": round(total_bytes / (total_ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
+           "layers": {}}
+    res["frac"] = round(res["achieved_GBs"] / PEAK_HBM_GBS, 4)
+    for li, (name, K, N, x1, q, y, ws, byts) in enumerate(layers):
+        us = float(np.median([evs[it][li][0].elapsed_time(evs[it][li][1]) for it in range(iters)])) * 1e3
+        res["layers"][name] = {"us": round(us, 2), "GBs": round(byts / (us * 1e-6) / 1e9, 1)}
+    log(f"[bench] gemv block {res['block_us']} us -> {res['achieved_GBs']} GB/s ({100 * res['frac']:.1f}% of HBM)")
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -65,7 +65,7 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
                const awq_qconfig* cfg, void* workspace, size_t ws_bytes, double* losses, int32_t* best,
                float* s_best, void* stream) {
     if (!X_bf16 || !W_bf16 || !mean_abs || !losses || !best || !s_best) return AWQ_ERR_INVALID_ARG;
-    if (T <= 0 || K <= 0 || N <= 0 || T > kIntMax || K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (T <= 0 || K <= 0 || N <= 0 || T * K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
     int st = check_cfg(cfg, K);
     if (st != AWQ_OK) return st;
     if (!aligned(X_bf16, 16) || !aligned(W_bf16, 2) || !aligned(mean_abs, 4) || !aligned(losses, 8) ||

@@ -33,41 +33,114 @@
 namespace awq {
 
 // Matrix-core operand layout used throughout (v_mfma_f32_16x16x32_bf16):
-//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) .. +7
-//   B (32 x 16): lane l holds column l%16, k = 8*(l/16) .. +7
+//   A (16 x 32): lane l holds row l%16 and 8 consecutive k of quad l/16
+//   B (32 x 16): lane l holds column l%16 and the same 8 k of quad l/16
 //   C (16 x 16): lane l holds column l%16, rows 4*(l/16) .. +3
-// A K chunk is 32 consecutive input channels; a group of G channels is G/32 chunks.
+// A K chunk is 32 input channels; a group of G channels is G/32 chunks.  Which 8 channels quad q
+// of chunk c holds is a permutation internal to the kernel (the sum over k does not depend on
+// it), chosen so that one X row's channels are read as whole 128-byte lines: for G >= 64, chunks
+// pair up and quad q of chunk c holds k = 64*(c/2) + 16*q + 8*(c%2) + e, so the four lanes of a
+// row read 2 x 64 contiguous bytes with two back-to-back loads.  For G = 32 (one chunk per group)
+// quad q holds k = 8*q + e.  The W tiling, the scale rows and the X loads use the same map.
+template <int G>
+__device__ __forceinline__ int kmap(int c, int q) {
+    if constexpr (G >= 64) return 64 * (c >> 1) + 16 * q + 8 * (c & 1);
+    else return 8 * q;
+}
 
-// W [K, N] bf16 -> Wt: for column block nb (16 columns), chunk kc (32 channels) and lane l, the
-// 8 bf16 values W[32*kc + 8*(l/16) + e][16*nb + l%16], e = 0..7, as one 16-byte word.  Columns
-// beyond N are zero (a zero column quantizes to zero error).
+// W [K, N] bf16 -> Wt (float32): for column block nb (16 columns), chunk kc (32 channels), half h
+// and lane l, the 4 float32 values W[G*(kc/C) + kmap(kc%C, l/16) + 4h + e][16*nb + l%16], e < 4,
+// as one 16-byte word (so a lane reads its 8 values of a chunk as two linear 16-byte words).
+// Columns beyond N are zero (a zero column quantizes to zero error).
+template <int G>
 __global__ __launch_bounds__(256) void k_tile_w(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                                int64_t total, u32x4* __restrict__ Wt) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                int64_t total, floatx4* __restrict__ Wt) {
+    constexpr int C = G / 32;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one (nb, kc, lane)
     if (e >= total) return;
     const int lane = (int)(e & 63);
     const int64_t rest = e >> 6;
     const int64_t kchunks = K / 32;
     const int64_t kc = rest % kchunks, nb = rest / kchunks;
-    const int64_t k0 = kc * 32 + 8 * (lane >> 4);
+    const int64_t k0 = (kc / C) * G + kmap<G>((int)(kc % C), lane >> 4);
     const int64_t n = nb * 16 + (lane & 15);
-    uint32_t v[4] = {0, 0, 0, 0};
-    if (n < N) {
+    float v[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-            v[h] = (uint32_t)W[(k0 + 2 * h) * N + n] | ((uint32_t)W[(k0 + 2 * h + 1) * N + n] << 16);
-    }
-    Wt[e] = u32x4{v[0], v[1], v[2], v[3]};
+    for (int i = 0; i < 8; ++i) v[i] = n < N ? bf16_lo((uint32_t)W[(k0 + i) * N + n]) : 0.f;
+    floatx4* dst = Wt + rest * 128 + lane;
+    dst[0] = floatx4{v[0], v[1], v[2], v[3]};
+    dst[64] = floatx4{v[4], v[5], v[6], v[7]};
+}
+
+// Three-input max/min (one VALU instruction each; the inputs are never NaN).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// Reduction over the four lanes l, l^16, l^32, l^48 (the four quads of one column) with the
+// gfx950 lane-swap instructions: each returns both halves of the exchange, which are combined
+// symmetrically, so the result is the same in every one of the four lanes.
+__device__ __forceinline__ float quad_max(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_min(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS-only workgroup barrier.  Every cross-wavefront exchange in the search goes through ds_write
+// (E tiles and staged E inputs), so waiting for this wavefront's LDS operations is enough; the
+// X fragments that are in flight towards LDS are private to their wavefront and are waited for
+// with counted vmcnt waits at their use, so the barrier must not drain them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Direct global -> LDS transfer of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
+// land at LDS address `lds + 16*l`.  Issued from inline asm so that the compiler does not track
+// it: every wait for these transfers is an explicit, counted s_waitcnt vmcnt(N) (vmcnt counts
+// vector-memory operations that complete in issue order).  M0 carries the LDS base; it is saved
+// and restored around the transfer, and one wait state separates the M0 write from its use.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int G, int NA, int RBW, int NW, bool ZP>
 __global__ __launch_bounds__(NW * 64, 1) void k_search(
-    const uint16_t* __restrict__ X, int T, int K, const u32x4* __restrict__ Wt, int NB,
+    const uint16_t* __restrict__ X, int T, int K, const floatx4* __restrict__ Wt, int NB,
     const float* __restrict__ s_tab, const float* __restrict__ inv_tab, int n_grid, int n_asplit,
     int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
     constexpr int C = G / 32;            // K chunks per group
     constexpr int BM = NW * RBW * 16;    // token rows per workgroup
-    constexpr int V = G / 4;             // group values per lane (one column, one quad)
+    constexpr int NWE = C * 128;         // 16-byte W entries of a group tile (float32)
+    constexpr int NSE = NA * G / 4;      // 16-byte entries of NA scale rows of one group
+    constexpr int NSTG = NWE + 2 * NSE;  // staged 16-byte entries per group
+    constexpr int NSTGP = 2 * NW * 64;   // staging entries incl. padding (two per thread)
+    constexpr int D = RBW;               // transfers per X chunk per wavefront
+    static_assert(NW == 8 && NA < NW && NSTG <= NSTGP, "tile shape");
 
     const int tile = xcd_tile(blockIdx.x, tiles_per_xcd);
     if (tile >= n_tiles) return;
@@ -76,13 +149,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     const int nb = rest % NB;
     const int tb = rest / NB;
     const int a0 = asplit * NA;
-    const int na = min(NA, n_grid - a0);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = lane >> 4, r16 = lane & 15;
     const int n_groups = K / G;
     const int kchunks = K / 32;
 
+    // X fragments: a two-slot ring per wavefront; slot s, row block rb, lane l holds the 16 bytes
+    // lane l feeds to the matrix core, so reads are linear (conflict-free) ds_read_b128.
+    __shared__ u32x4 Xs[NW][2][RBW][64];
+    // E tiles (bf16, B-operand layout), double buffered over groups.
     __shared__ u32x4 Es[2][NA][C][64];
+    // Staged inputs of the E computation of one group, double buffered: the W tile (float32, in
+    // B-operand order), then NA scale rows, then NA reciprocal rows (16-byte entries).
+    __shared__ u32x4 Stg[2][NSTGP];
     __shared__ double red[NW][NA];
 
     floatx4 acc[NA][RBW];
@@ -91,139 +170,197 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) acc[a][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // A-fragment sources: row = tile row of this lane in row block rb; rows >= T read row T-1
-    // (valid memory) and are zeroed.
-    const uint16_t* xrow[RBW];
-    bool rvalid[RBW];
+    // Rows >= T read row T-1 (valid memory); their products are masked out in the epilogue.
+    int xoff[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
         const int row = tb * BM + (wave * RBW + rb) * 16 + r16;
-        rvalid[rb] = row < T;
-        xrow[rb] = X + (int64_t)min(row, T - 1) * K + 8 * q;
+        xoff[rb] = min(row, T - 1) * K;
     }
-    auto load_A = [&](int kc, u32x4 (&A)[RBW]) {
+    // Start the transfer of X chunk kc (global chunk index) into ring slot `slot` (D transfers).
+    auto fetch_X = [&](int kc, int slot) {
+        const int k0 = (kc / C) * G + kmap<G>(kc % C, q);
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-            u32x4 v = *(const u32x4*)(xrow[rb] + kc * 32);
-            A[rb] = rvalid[rb] ? v : u32x4{0u, 0u, 0u, 0u};
+        for (int rb = 0; rb < RBW; ++rb)
+            dma16(X + xoff[rb] + k0, (uint32_t)(uintptr_t)&Xs[wave][slot][rb][0]);
+    };
+
+    // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
+    // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  The
+    // padding entries re-read the last valid entry.
+    auto stage = [&](int jg, int buf) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
+            const int es = e - NWE;
+            const int which = es >= NSE;                     // 0: scale row, 1: reciprocal row
+            const int idx = es - which * NSE;
+            const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
+            const float* srow = (which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + jg * G + off;
+            const void* src = e < NWE ? (const void*)(Wt + ((int64_t)nb * kchunks + (int64_t)jg * C) * 128 + e)
+                                      : (const void*)srow;
+            dma16(src, (uint32_t)(uintptr_t)&Stg[buf][wave * 64 + NW * 64 * r]);
         }
     };
 
-    // Quantize/dequantize the 16-column tile of group jg for alpha a0 + wave; write E (bf16) into
-    // Es[buf][wave] in B-operand layout.
-    auto compute_E = [&](int jg, int buf) {
-        const int a = a0 + wave;
-        const u32x4* wsrc = Wt + ((int64_t)nb * kchunks + (int64_t)jg * C) * 64 + lane;
-        u32x4 wv[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) wv[c] = wsrc[c * 64];
-        const float* srow = s_tab + (int64_t)a * K + jg * G + 8 * q;
-        const float* irow = inv_tab + (int64_t)a * K + jg * G + 8 * q;
-        float p[V];
+    // ---- E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].
+    // Lane (column r16, quad q) owns the G/4 values of its column in the quad's k positions of each
+    // chunk: p = s*w, the group max/min (in registers, then across the 4 lanes of the column), the
+    // step and zero, then per value: quantize, dequantize, subtract, unscale, round to bf16.
+    const int slot = min(wave, NA - 1);
+    auto compute_E = [&](int ibuf, int ebuf) {
+        // the inputs were staged at the top of the previous group step; C*D + 2 transfers follow
+        wait_vmcnt<C * D + 2>();
+        float p[C * 8];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const floatx4 s0 = *(const floatx4*)(srow + 32 * c);
-            const floatx4 s1 = *(const floatx4*)(srow + 32 * c + 4);
-            p[8 * c + 0] = s0[0] * bf16_lo(wv[c][0]);
-            p[8 * c + 1] = s0[1] * bf16_hi(wv[c][0]);
-            p[8 * c + 2] = s0[2] * bf16_lo(wv[c][1]);
-            p[8 * c + 3] = s0[3] * bf16_hi(wv[c][1]);
-            p[8 * c + 4] = s1[0] * bf16_lo(wv[c][2]);
-            p[8 * c + 5] = s1[1] * bf16_hi(wv[c][2]);
-            p[8 * c + 6] = s1[2] * bf16_lo(wv[c][3]);
-            p[8 * c + 7] = s1[3] * bf16_hi(wv[c][3]);
+            const floatx4 w0 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + lane]);
+            const floatx4 w1 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + 64 + lane]);
+            const floatx4 s0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4]);
+            const floatx4 s1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[8 * c + j] = s0[j] * w0[j];
+                p[8 * c + 4 + j] = s1[j] * w1[j];
+            }
         }
         float d, lo, hi;
         if (ZP) {
             float mx = 0.f, mn = 0.f;   // the group range always includes 0
 #pragma unroll
-            for (int i = 0; i < V; i += 2) {
-                mx = fmaxf(mx, fmaxf(p[i], p[i + 1]));
-                mn = fminf(mn, fminf(p[i], p[i + 1]));
+            for (int i = 0; i < C * 8; i += 2) {
+                mx = max3f(mx, p[i], p[i + 1]);
+                mn = min3f(mn, p[i], p[i + 1]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mn = fminf(mn, __shfl_xor(mn, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            mn = fminf(mn, __shfl_xor(mn, 32, 64));
-            d = (mx - mn) / 15.0f;
-            if (d == 0.f) d = 1.f;
-            const float z = fminf(fmaxf(rintf(-mn / d), 0.f), 15.f);
+            mx = quad_max(mx);
+            mn = quad_min(mn);
+            d = (mx - mn) * (1.0f / 15.0f);
+            d = d == 0.f ? 1.f : d;
+            const float z = __builtin_amdgcn_fmed3f(rintf(-mn * __builtin_amdgcn_rcpf(d)), 0.f, 15.f);
             lo = -z;
             hi = 15.f - z;
         } else {
             float am = 0.f;
 #pragma unroll
-            for (int i = 0; i < V; i += 2) am = fmaxf(am, fmaxf(fabsf(p[i]), fabsf(p[i + 1])));
-            am = fmaxf(am, __shfl_xor(am, 16, 64));
-            am = fmaxf(am, __shfl_xor(am, 32, 64));
-            d = am / 7.0f;
-            if (d == 0.f) d = 1.f;
+            for (int i = 0; i < C * 8; i += 2) am = max3f(am, fabsf(p[i]), fabsf(p[i + 1]));
+            am = quad_max(am);
+            d = am * (1.0f / 7.0f);
+            d = d == 0.f ? 1.f : d;
             lo = -7.f;
             hi = 7.f;
         }
-        const float rd = 1.0f / d;
+        const float rd = __builtin_amdgcn_rcpf(d);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const floatx4 i0 = *(const floatx4*)(irow + 32 * c);
-            const floatx4 i1 = *(const floatx4*)(irow + 32 * c + 4);
+            const floatx4 i0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4]);
+            const floatx4 i1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
             float e[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float pv = p[8 * c + j];
-                const float lv = fminf(fmaxf(rintf(pv * rd), lo), hi);
-                const float es = fmaf(lv, d, -pv);          // quantization error in the scaled domain
-                e[j] = es * (j < 4 ? i0[j & 3] : i1[j & 3]);  // back to the original domain
+                const float lv = __builtin_amdgcn_fmed3f(rintf(pv * rd), lo, hi);
+                e[j] = fmaf(lv, d, -pv) * (j < 4 ? i0[j] : i1[j - 4]);   // (q*Delta - s*w) / s
             }
-            Es[buf][wave][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                                           pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+            if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
+                Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                                                pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
         }
     };
 
-    if (wave < na) compute_E(0, 0);
-    __syncthreads();
-
-    u32x4 A[RBW], An[RBW];
-    load_A(0, A);
-    for (int jg = 0; jg < n_groups; ++jg) {
-        const int buf = jg & 1;
+    // Matrix-core work of one group: for each chunk, read the X fragments from this wavefront's
+    // ring slot, issue the MFMAs, and once the slot has been read start the transfer of the chunk
+    // two ahead into it.  The E fragments (one per alpha, already in LDS since the last barrier)
+    // of the next chunk are read while the current chunk's MFMAs issue.
+    auto mfma_group = [&](int jg, int buf) {
+        u32x4 B[2][NA];   // E fragments of chunks c (B[c & 1]) and c + 1 (B[(c + 1) & 1])
+#pragma unroll
+        for (int a = 0; a < NA; ++a) B[0][a] = Es[buf][a][0][lane];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int kc_next = jg * C + c + 1;
-            if (kc_next < kchunks) load_A(kc_next, An);
+            const int kc = jg * C + c;
+            const int xs = C >= 2 ? (c & 1) : (jg & 1);
+            u32x4 A[RBW];
+            // transfers issued after this chunk's: see the issue order described at the main loop
+            if constexpr (C == 1) wait_vmcnt<D + 4>();
+            else if (c < 2) wait_vmcnt<D + 2>();
+            else wait_vmcnt<D>();
 #pragma unroll
-            for (int a = 0; a < NA; ++a) {
-                if (a < na) {
-                    const u32x4 bw = Es[buf][a][c][lane];
-                    const bf16x8 B = __builtin_bit_cast(bf16x8, bw);
+            for (int rb = 0; rb < RBW; ++rb) A[rb] = Xs[wave][xs][rb][lane];
+            if (c + 1 < C) {
 #pragma unroll
-                    for (int rb = 0; rb < RBW; ++rb)
-                        acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, A[rb]), B, acc[a][rb]);
-                }
+                for (int a = 0; a < NA; ++a) B[(c + 1) & 1][a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
             }
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) A[rb] = An[rb];
+            for (int a = 0; a < NA; ++a) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+                    acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, A[rb]), __builtin_bit_cast(bf16x8, B[c & 1][a]),
+                                              acc[a][rb]);
+                if (a == 0) fetch_X(min(kc + 2, kchunks - 1), xs);   // the slot's data is in registers now
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep each chunk's fragments short-lived
         }
-        if (jg + 1 < n_groups && wave < na) compute_E(jg + 1, buf ^ 1);
-        __syncthreads();
-    }
+    };
 
-    // Epilogue: sum of squares per alpha; fixed-order reductions (lanes, then wavefronts).
+    // ---- prologue: X chunks 0 and 1 in flight, inputs of groups 0 and 1 staged, E(0) computed.
+    fetch_X(0, 0);
+    fetch_X(min(1, kchunks - 1), 1);
+    stage(0, 0);
+    stage(min(1, n_groups - 1), 1);
+    wait_vmcnt<0>();
+    lds_barrier();
+    compute_E(0, 0);
+    lds_barrier();
+
+    // Main loop.  The two wavefronts that share a SIMD (w and w + 4) run the two halves of a
+    // group step in opposite order: wavefronts 0-3 issue their X.E(jg) matrix-core work first and
+    // then compute their E(jg+1) tile; wavefronts 4-7 compute E(jg+1) first and then issue their
+    // matrix-core work.  Both halves only read E(jg) and write E(jg+1), so the order is free, and
+    // on every SIMD one wavefront keeps the matrix core busy while the other uses the VALU.
+    // Transfer issue order of a wavefront in step jg (both halves issue the same sequence):
+    //   stage(jg + 2) [2], then after reading X chunk c of this group, chunk c + 2 [D each].
+    // Hence X chunk c of group jg was followed by D + 2 transfers when c < 2 (it was issued in the
+    // previous step, before stage(jg + 2)), by D when c >= 2, and by D + 4 when a group is a
+    // single chunk; the staged inputs of group jg + 1 were followed by C*D + 2 (one step of X
+    // chunks and one staging).  Counts only grow in the first steps, where the prologue waited.
+    const bool mfma_first = (wave & 4) == 0;
+    for (int jg = 0; jg < n_groups; ++jg) {
+        const int buf = jg & 1;
+        // Stg[buf] held the inputs of group jg, consumed by E(jg) in the previous step
+        stage(min(jg + 2, n_groups - 1), buf);
+        if (mfma_first) {
+            mfma_group(jg, buf);
+            compute_E(buf ^ 1, buf ^ 1);
+        } else {
+            compute_E(buf ^ 1, buf ^ 1);
+            mfma_group(jg, buf);
+        }
+        lds_barrier();
+    }
+    // drain the trailing (redundant) transfers before the LDS is reused or released
+    wait_vmcnt<0>();
+
+    // ---- epilogue: sum of squares per alpha over valid rows; fixed-order reductions.
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         float ss = 0.f;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ss = fmaf(acc[a][rb][i], acc[a][rb][i], ss);
+            for (int i = 0; i < 4; ++i) {
+                const int row = tb * BM + (wave * RBW + rb) * 16 + 4 * q + i;
+                const float v = row < T ? acc[a][rb][i] : 0.f;
+                ss = fmaf(v, v, ss);
+            }
         const double t = wave_sum((double)ss);
         if (lane == 0) red[wave][a] = t;
     }
     __syncthreads();
-    if (threadIdx.x < na) {
-        double s = 0.0;
+    if (threadIdx.x < NA && a0 + (int)threadIdx.x < n_grid) {
+        double sum = 0.0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) s += red[w][threadIdx.x];
-        partials[((int64_t)tb * NB + nb) * n_grid + a0 + threadIdx.x] = s;
+        for (int w = 0; w < NW; ++w) sum += red[w][threadIdx.x];
+        partials[((int64_t)tb * NB + nb) * n_grid + a0 + threadIdx.x] = sum;
     }
 }
 
@@ -269,7 +406,7 @@ namespace {
 constexpr int kNA = 7, kRBW = 4, kNW = 8;
 constexpr int kBM = kNW * kRBW * 16;
 
-typedef void (*search_fn)(const uint16_t*, int, int, const u32x4*, int, const float*, const float*, int,
+typedef void (*search_fn)(const uint16_t*, int, int, const floatx4*, int, const float*, const float*, int,
                           int, int, int, double*);
 
 search_fn pick(int g, int zp) {
@@ -306,7 +443,7 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     size_t off = 0;
     p.off_s = off;    off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_inv = off;  off = align256(off + (size_t)n_grid * K * sizeof(float));
-    p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(uint16_t));
+    p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(float));
     p.off_part = off; off = align256(off + (size_t)p.tb * p.nb * n_grid * sizeof(double));
     p.ws_bytes = off;
     return p;
@@ -318,13 +455,16 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     char* base = (char*)ws;
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
-    u32x4* Wt = (u32x4*)(base + p.off_wt);
+    floatx4* Wt = (floatx4*)(base + p.off_wt);
     double* part = (double*)(base + p.off_part);
 
     hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
     if (e != hipSuccess) return e;
     const int64_t total = p.nb * (K / 32) * 64;
-    k_tile_w<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(W, K, N, total, Wt);
+    const unsigned tgrid = (unsigned)((total + 255) / 256);
+    if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     search_fn fn = pick(p.group_size, p.zero_point);
     if (!fn) return hipErrorInvalidValue;
