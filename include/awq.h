@@ -134,9 +134,8 @@ int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq
  * on chip and multiplied with 16-bit activations).
  *   X  bf16 [M, K];  s  float32 [K];  codes/scales/zeros as written by awq_pack;
  *   Y  bf16 [M, N] out.  Accumulation is float32; x/s is rounded to bf16 once.
- *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes.  It holds
- *   split-K partials and arrival counters: it must be zero-filled before its first use,
- *   and every completed call leaves the counters at zero again.
+ *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes (float32 split-K
+ *   partials; no initialization needed; the size may be 0).
  * Requires N % 8 == 0.
  */
 size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size);

@@ -95,6 +95,113 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
         }
 }
 
+// ---------------------------------------------------------------- M = 1: decode-shaped GEMV
+// HBM-bound: every byte of packed weights is read once.  A wavefront owns 256 output columns and
+// one quantization group (G rows).  Each lane reads 4 adjacent columns x 8 rows of codes with one
+// 16-byte load per code row (a wavefront reads 1 KB of one code row: fully coalesced) and issues
+// all G/8 loads of its group before consuming them.  Nibbles k and k+4 of a code word become two
+// bf16 values 128 + q with one and-or (plus one shift), and v_dot2c_f32_bf16 multiplies them with
+// the pair (x'_k, x'_{k+4}) of activations x' = bf16(x/s) staged in LDS in that pair order.  The
+// offset and the zero point come out once per group: sum (q - z) x' = sum (128 + q) x' -
+// (128 + z) sum x', where sum x' adds the same bf16-rounded values the products used.
+// The 4 wavefronts of a workgroup take 4 consecutive groups and reduce through LDS in a fixed
+// order; workgroups along K write float32 partials with plain stores and a second small kernel
+// adds them in a fixed order and writes the bf16 outputs.  (A last-arriving-workgroup handoff
+// inside one kernel would need device-scope release/acquire, which on this multi-die GPU writes
+// back and invalidates a whole L2 per workgroup.)  No atomics: results are deterministic.
+constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
+constexpr int kGemvWaves = 4;    // groups per workgroup
+
+template <int G>
+__global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
+                                                    const uint32_t* __restrict__ codes,
+                                                    const float* __restrict__ scales,
+                                                    const uint8_t* __restrict__ zeros, int K, int N,
+                                                    uint16_t* __restrict__ Y, float* __restrict__ part) {
+    constexpr int R = G / 8;                     // code rows per group
+    __shared__ uint32_t xpair[kGemvWaves][G / 2]; // code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
+    __shared__ float sxs[kGemvWaves];
+    __shared__ float red[kGemvWaves][kGemvCols];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
+    const int n_groups = K / G;
+    const int g = kb * kGemvWaves + wave;
+    const bool gvalid = g < n_groups;
+    const int gg = gvalid ? g : n_groups - 1;
+    const int n0 = cb * kGemvCols + lane * 4;
+    const bool nvalid = n0 < N;                  // N % 4 == 0
+    const int nc = nvalid ? n0 : N - 4;
+
+    // issue every code load of the group first (R x 16 bytes per lane in flight)
+    u32x4 cw[R];
+    const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cw[r] = *(const u32x4*)(cbase + (int64_t)r * N);
+    const floatx4 dsc = *(const floatx4*)(scales + (int64_t)gg * N + nc);
+    const uint32_t zw = *(const uint32_t*)(zeros + (int64_t)gg * N + nc);
+
+    // x' = bf16(x / s) of the group in pair order: lane l < G/2 forms pair l (row l/4, slot l%4)
+    float sx = 0.f;
+    if (lane < G / 2) {
+        const int r = lane >> 2, j = lane & 3;
+        const int k1 = gg * G + 8 * r + j, k2 = k1 + 4;
+        const __bf16 b1 = (__bf16)(bf16_lo((uint32_t)X[k1]) / s[k1]);
+        const __bf16 b2 = (__bf16)(bf16_lo((uint32_t)X[k2]) / s[k2]);
+        sx = (float)b1 + (float)b2;
+        xpair[wave][lane] = (uint32_t)__builtin_bit_cast(unsigned short, b1) |
+                            ((uint32_t)__builtin_bit_cast(unsigned short, b2) << 16);
+    }
+    sx = wave_sum(sx);
+    if (lane == 0) sxs[wave] = sx;
+    __syncthreads();
+
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t xp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xp[j] = xpair[wave][4 * r + j];   // broadcast reads
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t w = cw[r][c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t h = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u;   // bf16 (128+q_j, 128+q_{j+4})
+                acc[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
+                                                         __builtin_bit_cast(bf16x2_t, xp[j]), acc[c], false);
+            }
+        }
+    }
+    const float sxw = sxs[wave];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float z = (float)((zw >> (8 * c)) & 0xFFu);
+        red[wave][lane * 4 + c] = gvalid ? dsc[c] * fmaf(-(128.f + z), sxw, acc[c]) : 0.f;
+    }
+    __syncthreads();
+    const int col = cb * kGemvCols + (int)threadIdx.x;
+    const float ps = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
+    if (col >= N) return;
+    if (nkb == 1) {
+        const __bf16 o = (__bf16)ps;
+        Y[col] = __builtin_bit_cast(uint16_t, o);
+    } else {
+        part[(int64_t)kb * N + col] = ps;
+    }
+}
+
+// Y[n] = bf16(sum_b part[b][n]) in a fixed order.
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int nkb, int N,
+                                                     uint16_t* __restrict__ Y) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float t = 0.f;
+    for (int b = 0; b < nkb; ++b) t += part[(int64_t)b * N + n];
+    const __bf16 o = (__bf16)t;
+    Y[n] = __builtin_bit_cast(uint16_t, o);
+}
+
 namespace {
 typedef void (*gemm_fn)(const uint16_t*, int64_t, const float*, const uint32_t*, const float*, const uint8_t*,
                         int64_t, int64_t, uint16_t*);
@@ -108,9 +215,18 @@ gemm_fn pick_g(int g) {
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
-    (void)K;
-    (void)group_size;
     GemmPlan p{};
+    if (M == 1) {
+        p.variant = 0;
+        p.grid_x = (N + kGemvCols - 1) / kGemvCols;
+        p.grid_y = (K / group_size + kGemvWaves - 1) / kGemvWaves;
+        p.grid_z = 1;
+        p.ksplit = (int)p.grid_y;
+        p.off_part = 0;
+        p.off_cnt = 0;
+        p.ws_bytes = p.grid_y > 1 ? (size_t)p.grid_y * N * sizeof(float) : 0;
+        return p;
+    }
     p.variant = M <= 16 ? 1 : 4;
     p.grid_x = (N + 63) / 64;
     p.grid_y = (M + 16 * p.variant - 1) / (16 * p.variant);
@@ -125,7 +241,20 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes,
                        const float* scales, const uint8_t* zeros, int64_t K, int64_t N, int group_size,
                        uint16_t* Y, void* ws, const GemmPlan& p, hipStream_t st) {
-    (void)ws;
+    if (p.variant == 0) {
+        float* part = (float*)((char*)ws + p.off_part);
+        dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
+        if (group_size == 32)
+            k_w4a16_gemv<32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        else if (group_size == 64)
+            k_w4a16_gemv<64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        else
+            k_w4a16_gemv<128><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.grid_y == 1) return e;
+        k_gemv_reduce<<<(unsigned)((N + 255) / 256), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);
+        return hipGetLastError();
+    }
     gemm_fn fn = p.variant == 1 ? pick_g<1>(group_size) : pick_g<4>(group_size);
     if (!fn) return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
