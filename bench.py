@@ -49,11 +49,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--gemv-iters", type=int, default=50)
-    ap.add_argument("--cpu-cols", type=int, default=1024,
+    ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns of the oracle's bounded sample (of 4096)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of known size (for HBM counter calibration)")
     return ap.parse_args()
+
+
+def search_traffic():
+    """HBM-side bytes per search launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (scaled by the copy-kernel calibration), or None once the kernel source changed since then."""
+    import hashlib
+    prof = os.path.join(HERE, "profiles", "search_c2_hbm_traffic.md")
+    try:
+        text = open(prof, encoding="utf-8").read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        src = b"".join(open(os.path.join(HERE, "weight_only_int4_act_amd", "csrc", f), "rb").read()
+                       for f in ("awq_search.hip", "awq_device.h"))
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return float(rec["bytes_per_launch"])
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(layer, n_cols):
@@ -173,7 +190,7 @@ def main():
                    "T": T, "K": K, "N": N, "group_size": g, "zero_point": True, "n_grid": 21},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": search_traffic(),
                      "kernel": "awq_search call (k_search fused loss kernel + scale table, W tiling, loss "
                                "reduction and argmin kernels)",
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(search_ms, 4)},

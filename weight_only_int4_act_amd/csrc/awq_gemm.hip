@@ -197,7 +197,13 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     float t = 0.f;
-    for (int b = 0; b < nkb; ++b) t += part[(int64_t)b * N + n];
+    for (int b0 = 0; b0 < nkb; b0 += 8) {   // 8 loads in flight, added in the same fixed order
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = b0 + j < nkb ? part[(int64_t)(b0 + j) * N + n] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t += v[j];
+    }
     const __bf16 o = (__bf16)t;
     Y[n] = __builtin_bit_cast(uint16_t, o);
 }

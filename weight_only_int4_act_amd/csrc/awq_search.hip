@@ -371,7 +371,13 @@ __global__ __launch_bounds__(256) void k_reduce_losses(const double* __restrict_
     __shared__ double sm[256];
     const int i = blockIdx.x;
     double s = 0.0;
-    for (int64_t t = threadIdx.x; t < tiles; t += 256) s += partials[t * n_grid + i];
+    for (int64_t t0 = threadIdx.x; t0 < tiles; t0 += 8 * 256) {   // 8 loads in flight, fixed order
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = t0 + 256 * j < tiles ? partials[(t0 + 256 * j) * n_grid + i] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += v[j];
+    }
     sm[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {

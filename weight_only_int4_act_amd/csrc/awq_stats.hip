@@ -78,7 +78,13 @@ __global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ 
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= K) return;
     double s = 0.0;
-    for (int64_t c = 0; c < chunks; ++c) s += partial[c * K + k];
+    for (int64_t c0 = 0; c0 < chunks; c0 += 8) {   // 8 loads in flight, added in the same fixed order
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = c0 + j < chunks ? partial[(c0 + j) * K + k] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += v[j];
+    }
     if (accumulate) s = sum_abs[k] + s;
     sum_abs[k] = s;
     if (mean_abs) mean_abs[k] = (float)(s / (double)total_tokens);
