@@ -72,7 +72,8 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
         !aligned(best, 4) || !aligned(s_best, 4))
         return AWQ_ERR_INVALID_ARG;
     const awq::SearchPlan p = awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid);
-    if (p.tiles > kIntMax) return AWQ_ERR_INVALID_ARG;
+    // tile counts and the 16-byte index into the tiled copy of X are 32-bit in the kernel
+    if (p.tiles > kIntMax || p.tb * p.bm * K / 8 > kIntMax) return AWQ_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs, p,

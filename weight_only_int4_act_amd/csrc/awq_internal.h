@@ -33,7 +33,7 @@ struct SearchPlan {
     int64_t tb;              // token blocks
     int64_t tiles, tiles_per_xcd, grid;
     // workspace layout (byte offsets)
-    size_t off_s, off_inv, off_wt, off_part, ws_bytes;
+    size_t off_s, off_inv, off_wt, off_xt, off_part, ws_bytes;
 };
 SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid);
 hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,

@@ -72,6 +72,26 @@ __global__ __launch_bounds__(256) void k_tile_w(const uint16_t* __restrict__ W, 
     dst[64] = floatx4{v[4], v[5], v[6], v[7]};
 }
 
+// X [T, K] bf16 -> Xt: for 16-row block R, chunk kc and lane l, the 16 bytes lane l feeds to the
+// matrix core as A operand: X[16R + l%16][G*(kc/C) + kmap(kc%C, l/16) + e], e < 8, stored at
+// Xt[(R*kchunks + kc)*64 + l].  Rows >= T are zero.  In this order every X fragment the search
+// loads is one contiguous 1 KB block (8 whole cache lines); read in place, a fragment touches 16
+// lines and uses half of each, which halves the rate at which the memory pipeline delivers X.
+template <int G>
+__global__ __launch_bounds__(256) void k_tile_x(const uint16_t* __restrict__ X, int64_t T, int64_t K,
+                                                int64_t total, u32x4* __restrict__ Xt) {
+    constexpr int C = G / 32;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one (R, kc, lane)
+    if (e >= total) return;
+    const int lane = (int)(e & 63);
+    const int64_t rest = e >> 6;
+    const int64_t kchunks = K / 32;
+    const int64_t kc = rest % kchunks, R = rest / kchunks;
+    const int64_t row = R * 16 + (lane & 15);
+    const int64_t k0 = (kc / C) * G + kmap<G>((int)(kc % C), lane >> 4);
+    Xt[e] = row < T ? *(const u32x4*)(X + row * K + k0) : u32x4{0u, 0u, 0u, 0u};
+}
+
 // Three-input max/min (one VALU instruction each; the inputs are never NaN).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     float r;
@@ -130,7 +150,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int G, int NA, int RBW, int NW, bool ZP>
 __global__ __launch_bounds__(NW * 64, 1) void k_search(
-    const uint16_t* __restrict__ X, int T, int K, const floatx4* __restrict__ Wt, int NB,
+    const u32x4* __restrict__ Xt, int T, int K, const floatx4* __restrict__ Wt, int NB,
     const float* __restrict__ s_tab, const float* __restrict__ inv_tab, int n_grid, int n_asplit,
     int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
     constexpr int C = G / 32;            // K chunks per group
@@ -139,7 +159,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     constexpr int NSE = NA * G / 4;      // 16-byte entries of NA scale rows of one group
     constexpr int NSTG = NWE + 2 * NSE;  // staged 16-byte entries per group
     constexpr int NSTGP = 2 * NW * 64;   // staging entries incl. padding (two per thread)
-    constexpr int D = RBW;               // transfers per X chunk per wavefront
     static_assert(NW == 8 && NA < NW && NSTG <= NSTGP, "tile shape");
 
     const int tile = xcd_tile(blockIdx.x, tiles_per_xcd);
@@ -154,9 +173,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     const int n_groups = K / G;
     const int kchunks = K / 32;
 
-    // X fragments: a two-slot ring per wavefront; slot s, row block rb, lane l holds the 16 bytes
-    // lane l feeds to the matrix core, so reads are linear (conflict-free) ds_read_b128.
-    __shared__ u32x4 Xs[NW][2][RBW][64];
     // E tiles (bf16, B-operand layout), double buffered over groups.
     __shared__ u32x4 Es[2][NA][C][64];
     // Staged inputs of the E computation of one group, double buffered: the W tile (float32, in
@@ -170,19 +186,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) acc[a][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Rows >= T read row T-1 (valid memory); their products are masked out in the epilogue.
+    // X fragments of this wavefront's rows for one whole group (C chunks x RBW row blocks), held in
+    // registers and loaded one group ahead: once the matrix-core work of chunk c of group jg has
+    // been issued, the same fragments receive chunk c of group jg + 1.  A load therefore has a whole
+    // group step to arrive.  Each load is one contiguous 1 KB block of the tiled X.
     int xoff[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-        const int row = tb * BM + (wave * RBW + rb) * 16 + r16;
-        xoff[rb] = min(row, T - 1) * K;
-    }
-    // Start the transfer of X chunk kc (global chunk index) into ring slot `slot` (D transfers).
-    auto fetch_X = [&](int kc, int slot) {
-        const int k0 = (kc / C) * G + kmap<G>(kc % C, q);
+    for (int rb = 0; rb < RBW; ++rb) xoff[rb] = (tb * (BM / 16) + wave * RBW + rb) * kchunks * 64 + lane;
+    u32x4 xr[C][RBW];
+    auto load_X = [&](int jg, int c) {
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-            dma16(X + xoff[rb] + k0, (uint32_t)(uintptr_t)&Xs[wave][slot][rb][0]);
+        for (int rb = 0; rb < RBW; ++rb) xr[c][rb] = Xt[xoff[rb] + (jg * C + c) * 64];
     };
 
     // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
@@ -208,30 +222,45 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // chunk: p = s*w, the group max/min (in registers, then across the 4 lanes of the column), the
     // step and zero, then per value: quantize, dequantize, subtract, unscale, round to bf16.
     const int slot = min(wave, NA - 1);
+    // p = s*w of chunk c (8 values of this lane).
+    auto load_p = [&](int ibuf, int c, float* pc) {
+        const floatx4 w0 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + lane]);
+        const floatx4 w1 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + 64 + lane]);
+        const floatx4 s0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4]);
+        const floatx4 s1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pc[j] = s0[j] * w0[j];
+            pc[4 + j] = s1[j] * w1[j];
+        }
+    };
+    // The X fragments of the next group occupy C*RBW*4 registers during the E computation, so the
+    // p values of the first C/2 chunks are not kept between the range pass and the quantization
+    // pass but formed again (the same products, so the same values).
+    constexpr int CR = C / 2;
     auto compute_E = [&](int ibuf, int ebuf) {
-        // the inputs were staged at the top of the previous group step; C*D + 2 transfers follow
-        wait_vmcnt<C * D + 2>();
-        float p[C * 8];
+        float pk[(C - CR) * 8];
+        float mx = 0.f, mn = 0.f;   // ZP: the group range always includes 0; else mx = max|p|
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const floatx4 w0 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + lane]);
-            const floatx4 w1 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + 64 + lane]);
-            const floatx4 s0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4]);
-            const floatx4 s1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
+            float pc[8];
+            load_p(ibuf, c, pc);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                p[8 * c + j] = s0[j] * w0[j];
-                p[8 * c + 4 + j] = s1[j] * w1[j];
+            for (int i = 0; i < 8; i += 2) {
+                if (ZP) {
+                    mx = max3f(mx, pc[i], pc[i + 1]);
+                    mn = min3f(mn, pc[i], pc[i + 1]);
+                } else {
+                    mx = max3f(mx, fabsf(pc[i]), fabsf(pc[i + 1]));
+                }
+            }
+            if (c >= CR) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pk[(c - CR) * 8 + j] = pc[j];
             }
         }
         float d, lo, hi;
         if (ZP) {
-            float mx = 0.f, mn = 0.f;   // the group range always includes 0
-#pragma unroll
-            for (int i = 0; i < C * 8; i += 2) {
-                mx = max3f(mx, p[i], p[i + 1]);
-                mn = min3f(mn, p[i], p[i + 1]);
-            }
             mx = quad_max(mx);
             mn = quad_min(mn);
             d = (mx - mn) * (1.0f / 15.0f);
@@ -240,11 +269,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             lo = -z;
             hi = 15.f - z;
         } else {
-            float am = 0.f;
-#pragma unroll
-            for (int i = 0; i < C * 8; i += 2) am = max3f(am, fabsf(p[i]), fabsf(p[i + 1]));
-            am = quad_max(am);
-            d = am * (1.0f / 7.0f);
+            mx = quad_max(mx);
+            d = mx * (1.0f / 7.0f);
             d = d == 0.f ? 1.f : d;
             lo = -7.f;
             hi = 7.f;
@@ -252,14 +278,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const float rd = __builtin_amdgcn_rcpf(d);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
+            float pc[8];
+            if (c < CR) {
+                load_p(ibuf, c, pc);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pc[j] = pk[(c - CR) * 8 + j];
+            }
             const floatx4 i0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4]);
             const floatx4 i1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
             float e[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float pv = p[8 * c + j];
-                const float lv = __builtin_amdgcn_fmed3f(rintf(pv * rd), lo, hi);
-                e[j] = fmaf(lv, d, -pv) * (j < 4 ? i0[j] : i1[j - 4]);   // (q*Delta - s*w) / s
+                const float lv = __builtin_amdgcn_fmed3f(rintf(pc[j] * rd), lo, hi);
+                e[j] = fmaf(lv, d, -pc[j]) * (j < 4 ? i0[j] : i1[j - 4]);   // (q*Delta - s*w) / s
             }
             if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
                 Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
@@ -267,44 +299,41 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         }
     };
 
-    // Matrix-core work of one group: for each chunk, read the X fragments from this wavefront's
-    // ring slot, issue the MFMAs, and once the slot has been read start the transfer of the chunk
-    // two ahead into it.  The E fragments (one per alpha, already in LDS since the last barrier)
-    // of the next chunk are read while the current chunk's MFMAs issue.
+    // Matrix-core work of one group: for each chunk and alpha, the RBW products with this wavefront's
+    // X fragments; the E fragment of an alpha for the next chunk is read from LDS as soon as the
+    // current one has been consumed, and the X fragments of a chunk are reloaded with the next
+    // group's as soon as its products have been issued.
     auto mfma_group = [&](int jg, int buf) {
-        u32x4 B[2][NA];   // E fragments of chunks c (B[c & 1]) and c + 1 (B[(c + 1) & 1])
+        const int jn = min(jg + 1, n_groups - 1);
+        u32x4 B[NA];
 #pragma unroll
-        for (int a = 0; a < NA; ++a) B[0][a] = Es[buf][a][0][lane];
+        for (int a = 0; a < NA; ++a) B[a] = Es[buf][a][0][lane];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int kc = jg * C + c;
-            const int xs = C >= 2 ? (c & 1) : (jg & 1);
-            u32x4 A[RBW];
-            // transfers issued after this chunk's: see the issue order described at the main loop
-            if constexpr (C == 1) wait_vmcnt<D + 4>();
-            else if (c < 2) wait_vmcnt<D + 2>();
-            else wait_vmcnt<D>();
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) A[rb] = Xs[wave][xs][rb][lane];
-            if (c + 1 < C) {
-#pragma unroll
-                for (int a = 0; a < NA; ++a) B[(c + 1) & 1][a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
-            }
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb)
-                    acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, A[rb]), __builtin_bit_cast(bf16x8, B[c & 1][a]),
+                    acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, xr[c][rb]), __builtin_bit_cast(bf16x8, B[a]),
                                               acc[a][rb]);
-                if (a == 0) fetch_X(min(kc + 2, kchunks - 1), xs);   // the slot's data is in registers now
+                if (c + 1 < C) B[a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep each chunk's fragments short-lived
+            load_X(jn, c);
+            // issue order inside the chunk: per alpha, its RBW products then the next chunk's E
+            // fragment read; the X reloads last.  Keeps one E fragment set and one X set live.
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                __builtin_amdgcn_sched_group_barrier(0x008, RBW, 0);   // MFMA
+                if (c + 1 < C) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // ---- prologue: X chunks 0 and 1 in flight, inputs of groups 0 and 1 staged, E(0) computed.
-    fetch_X(0, 0);
-    fetch_X(min(1, kchunks - 1), 1);
+    // ---- prologue: X of group 0 in registers, inputs of groups 0 and 1 staged, E(0) computed.
+#pragma unroll
+    for (int c = 0; c < C; ++c) load_X(0, c);
     stage(0, 0);
     stage(min(1, n_groups - 1), 1);
     wait_vmcnt<0>();
@@ -317,24 +346,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // then compute their E(jg+1) tile; wavefronts 4-7 compute E(jg+1) first and then issue their
     // matrix-core work.  Both halves only read E(jg) and write E(jg+1), so the order is free, and
     // on every SIMD one wavefront keeps the matrix core busy while the other uses the VALU.
-    // Transfer issue order of a wavefront in step jg (both halves issue the same sequence):
-    //   stage(jg + 2) [2], then after reading X chunk c of this group, chunk c + 2 [D each].
-    // Hence X chunk c of group jg was followed by D + 2 transfers when c < 2 (it was issued in the
-    // previous step, before stage(jg + 2)), by D when c >= 2, and by D + 4 when a group is a
-    // single chunk; the staged inputs of group jg + 1 were followed by C*D + 2 (one step of X
-    // chunks and one staging).  Counts only grow in the first steps, where the prologue waited.
+    // Vector-memory issue order of a wavefront: the X loads of group jg + 1 [C*RBW] inside the
+    // matrix-core half of step jg, and stage(jg + 2) [2 transfers] right before the E half.  So
+    // E(jg + 1), which reads the inputs staged in step jg - 1, finds C*RBW + 2 operations issued
+    // after them in both orders (vector-memory operations complete in issue order), and the
+    // compiler's own waits for the X registers, which cannot see the staging transfers, never
+    // wait for a staging transfer younger than one E half.  In step 0 the prologue has already
+    // waited for everything.
     const bool mfma_first = (wave & 4) == 0;
     for (int jg = 0; jg < n_groups; ++jg) {
         const int buf = jg & 1;
         // Stg[buf] held the inputs of group jg, consumed by E(jg) in the previous step
+        if (mfma_first) mfma_group(jg, buf);
         stage(min(jg + 2, n_groups - 1), buf);
-        if (mfma_first) {
-            mfma_group(jg, buf);
-            compute_E(buf ^ 1, buf ^ 1);
-        } else {
-            compute_E(buf ^ 1, buf ^ 1);
-            mfma_group(jg, buf);
-        }
+        wait_vmcnt<C * RBW + 2>();
+        compute_E(buf ^ 1, buf ^ 1);
+        if (!mfma_first) mfma_group(jg, buf);
         lds_barrier();
     }
     // drain the trailing (redundant) transfers before the LDS is reused or released
@@ -412,7 +439,7 @@ namespace {
 constexpr int kNA = 7, kRBW = 4, kNW = 8;
 constexpr int kBM = kNW * kRBW * 16;
 
-typedef void (*search_fn)(const uint16_t*, int, int, const floatx4*, int, const float*, const float*, int,
+typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, int,
                           int, int, int, double*);
 
 search_fn pick(int g, int zp) {
@@ -450,6 +477,7 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     p.off_s = off;    off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_inv = off;  off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(float));
+    p.off_xt = off;   off = align256(off + (size_t)p.tb * kBM * K * sizeof(uint16_t));
     p.off_part = off; off = align256(off + (size_t)p.tb * p.nb * n_grid * sizeof(double));
     p.ws_bytes = off;
     return p;
@@ -462,6 +490,7 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
     floatx4* Wt = (floatx4*)(base + p.off_wt);
+    u32x4* Xt = (u32x4*)(base + p.off_xt);
     double* part = (double*)(base + p.off_part);
 
     hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
@@ -472,9 +501,15 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
     else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t xtotal = p.tb * (kBM / 16) * (K / 32) * 64;
+    const unsigned xgrid = (unsigned)((xtotal + 255) / 256);
+    if (p.group_size == 32) k_tile_x<32><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
+    else if (p.group_size == 64) k_tile_x<64><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
+    else k_tile_x<128><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     search_fn fn = pick(p.group_size, p.zero_point);
     if (!fn) return hipErrorInvalidValue;
-    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(X, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, p.n_grid,
+    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, p.n_grid,
                                              p.n_asplit, (int)p.tiles, (int)p.tiles_per_xcd, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_reduce_losses<<<(unsigned)p.n_grid, 256, 0, st>>>(part, p.tb * p.nb, p.n_grid, losses);
