@@ -175,9 +175,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 
     // E tiles (bf16, B-operand layout), double buffered over groups.
     __shared__ u32x4 Es[2][NA][C][64];
-    // Staged inputs of the E computation of one group, double buffered: the W tile (float32, in
-    // B-operand order), then NA scale rows, then NA reciprocal rows (16-byte entries).
-    __shared__ u32x4 Stg[2][NSTGP];
+    // Staged inputs of the E computation of one group, triple buffered (group g in Stg[g % 3]): the
+    // W tile (float32, in B-operand order), then NA scale rows, then NA reciprocal rows (16-byte
+    // entries).
+    __shared__ u32x4 Stg[3][NSTGP];
     __shared__ double red[NW][NA];
 
     floatx4 acc[NA][RBW];
@@ -202,19 +203,29 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
     // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  The
     // padding entries re-read the last valid entry.
+    const char* stg_src[2];
+    int64_t stg_step[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
+        const int es = e - NWE;
+        const int which = es >= NSE;                     // 0: scale row, 1: reciprocal row
+        const int idx = es - which * NSE;
+        const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
+        if (e < NWE) {
+            stg_src[r] = (const char*)(Wt + (int64_t)nb * kchunks * 128 + e);
+            stg_step[r] = (int64_t)C * 128 * sizeof(floatx4);
+        } else {
+            stg_src[r] = (const char*)((which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + off);
+            stg_step[r] = (int64_t)G * sizeof(float);
+        }
+    }
+    const uint32_t stg_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&Stg[0][0]) +
+                             (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
     auto stage = [&](int jg, int buf) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
-            const int es = e - NWE;
-            const int which = es >= NSE;                     // 0: scale row, 1: reciprocal row
-            const int idx = es - which * NSE;
-            const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
-            const float* srow = (which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + jg * G + off;
-            const void* src = e < NWE ? (const void*)(Wt + ((int64_t)nb * kchunks + (int64_t)jg * C) * 128 + e)
-                                      : (const void*)srow;
-            dma16(src, (uint32_t)(uintptr_t)&Stg[buf][wave * 64 + NW * 64 * r]);
-        }
+        for (int r = 0; r < 2; ++r)
+            dma16(stg_src[r] + jg * stg_step[r], stg_lds + (uint32_t)(buf * NSTGP + NW * 64 * r) * 16);
     };
 
     // ---- E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].
@@ -222,77 +233,81 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // chunk: p = s*w, the group max/min (in registers, then across the 4 lanes of the column), the
     // step and zero, then per value: quantize, dequantize, subtract, unscale, round to bf16.
     const int slot = min(wave, NA - 1);
-    // p = s*w of chunk c (8 values of this lane).
-    auto load_p = [&](int ibuf, int c, float* pc) {
-        const floatx4 w0 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + lane]);
-        const floatx4 w1 = __builtin_bit_cast(floatx4, Stg[ibuf][c * 128 + 64 + lane]);
-        const floatx4 s0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4]);
-        const floatx4 s1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pc[j] = s0[j] * w0[j];
-            pc[4 + j] = s1[j] * w1[j];
-        }
-    };
-    // The X fragments of the next group occupy C*RBW*4 registers during the E computation, so the
-    // p values of the first C/2 chunks are not kept between the range pass and the quantization
-    // pass but formed again (the same products, so the same values).
-    constexpr int CR = C / 2;
+    // E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].  The
+    // level is rint(p/Delta) without the clamp to the code range: with Delta and the zero taken
+    // from the group's own max and min, the level leaves the range only when p/Delta lies at a .5
+    // tie at one end of the range, where either neighbour has the same |error| = Delta/2.  The loss
+    // is therefore unaffected up to the float32 rounding the search makes anyway; the packing
+    // kernel applies the quantizer exactly, clamp included.
+    // The staged inputs are read two chunks ahead of their use (the W tile and scale rows in the
+    // range pass, the reciprocal rows in the quantization pass), so that LDS latency overlaps the
+    // arithmetic of the previous chunk.
     auto compute_E = [&](int ibuf, int ebuf) {
-        float pk[(C - CR) * 8];
+        const u32x4* st = &Stg[ibuf][0];
+        const int srow = NWE + (slot * G) / 4;   // this slot's scale row
+        float pk[C * 8];
         float mx = 0.f, mn = 0.f;   // ZP: the group range always includes 0; else mx = max|p|
+        u32x4 in[2][4];             // W halves and scale halves of two chunks
+        auto fetch_in = [&](int c) {
+            in[c & 1][0] = st[c * 128 + lane];
+            in[c & 1][1] = st[c * 128 + 64 + lane];
+            in[c & 1][2] = st[srow + kmap<G>(c, q) / 4];
+            in[c & 1][3] = st[srow + kmap<G>(c, q) / 4 + 1];
+        };
+        fetch_in(0);
+        if constexpr (C > 1) fetch_in(1);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            float pc[8];
-            load_p(ibuf, c, pc);
+            const floatx4 w0 = __builtin_bit_cast(floatx4, in[c & 1][0]);
+            const floatx4 w1 = __builtin_bit_cast(floatx4, in[c & 1][1]);
+            const floatx4 s0 = __builtin_bit_cast(floatx4, in[c & 1][2]);
+            const floatx4 s1 = __builtin_bit_cast(floatx4, in[c & 1][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pk[c * 8 + j] = s0[j] * w0[j];
+                pk[c * 8 + 4 + j] = s1[j] * w1[j];
+            }
+            if (c + 2 < C) fetch_in(c + 2);
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
                 if (ZP) {
-                    mx = max3f(mx, pc[i], pc[i + 1]);
-                    mn = min3f(mn, pc[i], pc[i + 1]);
+                    mx = max3f(mx, pk[c * 8 + i], pk[c * 8 + i + 1]);
+                    mn = min3f(mn, pk[c * 8 + i], pk[c * 8 + i + 1]);
                 } else {
-                    mx = max3f(mx, fabsf(pc[i]), fabsf(pc[i + 1]));
+                    mx = max3f(mx, fabsf(pk[c * 8 + i]), fabsf(pk[c * 8 + i + 1]));
                 }
             }
-            if (c >= CR) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) pk[(c - CR) * 8 + j] = pc[j];
-            }
         }
-        float d, lo, hi;
+        u32x4 iv[2][2];             // reciprocal-row halves of two chunks
+        auto fetch_inv = [&](int c) {
+            iv[c & 1][0] = st[srow + NSE + kmap<G>(c, q) / 4];
+            iv[c & 1][1] = st[srow + NSE + kmap<G>(c, q) / 4 + 1];
+        };
+        fetch_inv(0);
+        if constexpr (C > 1) fetch_inv(1);
+        float d;
         if (ZP) {
             mx = quad_max(mx);
             mn = quad_min(mn);
             d = (mx - mn) * (1.0f / 15.0f);
-            d = d == 0.f ? 1.f : d;
-            const float z = __builtin_amdgcn_fmed3f(rintf(-mn * __builtin_amdgcn_rcpf(d)), 0.f, 15.f);
-            lo = -z;
-            hi = 15.f - z;
         } else {
             mx = quad_max(mx);
             d = mx * (1.0f / 7.0f);
-            d = d == 0.f ? 1.f : d;
-            lo = -7.f;
-            hi = 7.f;
         }
+        d = d == 0.f ? 1.f : d;
         const float rd = __builtin_amdgcn_rcpf(d);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            float pc[8];
-            if (c < CR) {
-                load_p(ibuf, c, pc);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) pc[j] = pk[(c - CR) * 8 + j];
-            }
-            const floatx4 i0 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4]);
-            const floatx4 i1 = __builtin_bit_cast(floatx4, Stg[ibuf][NWE + NSE + (slot * G + kmap<G>(c, q)) / 4 + 1]);
+            const floatx4 i0 = __builtin_bit_cast(floatx4, iv[c & 1][0]);
+            const floatx4 i1 = __builtin_bit_cast(floatx4, iv[c & 1][1]);
             float e[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float lv = __builtin_amdgcn_fmed3f(rintf(pc[j] * rd), lo, hi);
-                e[j] = fmaf(lv, d, -pc[j]) * (j < 4 ? i0[j] : i1[j - 4]);   // (q*Delta - s*w) / s
+                const float pv = pk[c * 8 + j];
+                const float lv = rintf(pv * rd);
+                e[j] = fmaf(lv, d, -pv) * (j < 4 ? i0[j] : i1[j - 4]);   // (level*Delta - s*w) / s
             }
+            if (c + 2 < C) fetch_inv(c + 2);
             if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
                 Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                                                 pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
@@ -301,13 +316,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 
     // Matrix-core work of one group: for each chunk and alpha, the RBW products with this wavefront's
     // X fragments; the E fragment of an alpha for the next chunk is read from LDS as soon as the
-    // current one has been consumed, and the X fragments of a chunk are reloaded with the next
-    // group's as soon as its products have been issued.
-    auto mfma_group = [&](int jg, int buf) {
+    // current one has been consumed, and the X fragments of chunk c < C-1 are reloaded with the next
+    // group's as soon as the chunk's products have been issued.  The last chunk of a group (when a
+    // group has several) is loaded at the start of the group's own matrix-core work instead, three
+    // chunks ahead of its use, so that its registers are free during the E computation.
+    constexpr int CL = C > 1 ? C - 1 : C;   // chunks loaded one group ahead
+    // The staging transfers of a step are issued inside the matrix-core half, after chunk SC, where
+    // their issue cost hides behind the matrix work; XS = X loads of the half issued before them.
+    constexpr int SC = C >= 4 ? 1 : 0;
+    constexpr int XS = (C > 1 ? RBW : 0) + (SC + 1) * RBW;
+    auto mfma_group = [&](int jg, int buf, int sjg, int sbuf) {
         const int jn = min(jg + 1, n_groups - 1);
+        if constexpr (C > 1) load_X(jg, C - 1);
         u32x4 B[NA];
 #pragma unroll
         for (int a = 0; a < NA; ++a) B[a] = Es[buf][a][0][lane];
+        if constexpr (C > 1) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);                         // DS read
 #pragma unroll
         for (int c = 0; c < C; ++c) {
 #pragma unroll
@@ -318,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                                               acc[a][rb]);
                 if (c + 1 < C) B[a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
             }
-            load_X(jn, c);
+            if (c < CL) load_X(jn, c);
             // issue order inside the chunk: per alpha, its RBW products then the next chunk's E
             // fragment read; the X reloads last.  Keeps one E fragment set and one X set live.
 #pragma unroll
@@ -326,16 +351,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                 __builtin_amdgcn_sched_group_barrier(0x008, RBW, 0);   // MFMA
                 if (c + 1 < C) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
+            if (c < CL) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
             __builtin_amdgcn_sched_barrier(0);
+            if (c == SC) stage(sjg, sbuf);
         }
     };
 
-    // ---- prologue: X of group 0 in registers, inputs of groups 0 and 1 staged, E(0) computed.
+    // ---- prologue: X of group 0 in registers, inputs of groups 0-2 staged, E(0) computed.
 #pragma unroll
-    for (int c = 0; c < C; ++c) load_X(0, c);
+    for (int c = 0; c < CL; ++c) load_X(0, c);
     stage(0, 0);
     stage(min(1, n_groups - 1), 1);
+    stage(min(2, n_groups - 1), 2);
     wait_vmcnt<0>();
     lds_barrier();
     compute_E(0, 0);
@@ -346,23 +373,31 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // then compute their E(jg+1) tile; wavefronts 4-7 compute E(jg+1) first and then issue their
     // matrix-core work.  Both halves only read E(jg) and write E(jg+1), so the order is free, and
     // on every SIMD one wavefront keeps the matrix core busy while the other uses the VALU.
-    // Vector-memory issue order of a wavefront: the X loads of group jg + 1 [C*RBW] inside the
-    // matrix-core half of step jg, and stage(jg + 2) [2 transfers] right before the E half.  So
-    // E(jg + 1), which reads the inputs staged in step jg - 1, finds C*RBW + 2 operations issued
-    // after them in both orders (vector-memory operations complete in issue order), and the
-    // compiler's own waits for the X registers, which cannot see the staging transfers, never
-    // wait for a staging transfer younger than one E half.  In step 0 the prologue has already
-    // waited for everything.
+    // Every wavefront issues stage(jg + 3) [2 transfers] inside its matrix-core half, which also
+    // issues C*RBW X loads (the last chunk of group jg, then the other chunks of group jg + 1), XS
+    // of them before the staging.  E(jg + 1) reads the inputs staged in step jg - 2; vector-memory
+    // operations complete in issue order, and after that staging a wavefront has issued the rest
+    // of that half, C*RBW - XS loads, then one more matrix-core half (C*RBW + 2 operations) if it
+    // computes E first in step jg, two if it computes E second.  The compiler's own waits for the
+    // X registers, which cannot see the staging transfers, wait at most for a staging issued one
+    // E half earlier.  In steps 0 and 1 the prologue has already waited for everything.
     const bool mfma_first = (wave & 4) == 0;
+    int sb = 0;   // jg % 3: Stg[sb] held group jg, consumed by E(jg) in the previous step
     for (int jg = 0; jg < n_groups; ++jg) {
         const int buf = jg & 1;
-        // Stg[buf] held the inputs of group jg, consumed by E(jg) in the previous step
-        if (mfma_first) mfma_group(jg, buf);
-        stage(min(jg + 2, n_groups - 1), buf);
-        wait_vmcnt<C * RBW + 2>();
-        compute_E(buf ^ 1, buf ^ 1);
-        if (!mfma_first) mfma_group(jg, buf);
+        const int sbn = sb == 2 ? 0 : sb + 1;   // (jg + 1) % 3
+        const int sjg = min(jg + 3, n_groups - 1);
+        if (mfma_first) {
+            mfma_group(jg, buf, sjg, sb);
+            wait_vmcnt<C * RBW - XS + 2 * (C * RBW + 2)>();
+            compute_E(sbn, buf ^ 1);
+        } else {
+            wait_vmcnt<C * RBW - XS + C * RBW + 2>();
+            compute_E(sbn, buf ^ 1);
+            mfma_group(jg, buf, sjg, sb);
+        }
         lds_barrier();
+        sb = sbn;
     }
     // drain the trailing (redundant) transfers before the LDS is reused or released
     wait_vmcnt<0>();
