@@ -256,6 +256,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         };
         fetch_in(0);
         if constexpr (C > 1) fetch_in(1);
+        float cmx[C], cmn[C];       // per-chunk range, combined below as a tree
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const floatx4 w0 = __builtin_bit_cast(floatx4, in[c & 1][0]);
@@ -268,15 +269,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                 pk[c * 8 + 4 + j] = s1[j] * w1[j];
             }
             if (c + 2 < C) fetch_in(c + 2);
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                if (ZP) {
-                    mx = max3f(mx, pk[c * 8 + i], pk[c * 8 + i + 1]);
-                    mn = min3f(mn, pk[c * 8 + i], pk[c * 8 + i + 1]);
-                } else {
-                    mx = max3f(mx, fabsf(pk[c * 8 + i]), fabsf(pk[c * 8 + i + 1]));
-                }
+            const float* v = &pk[c * 8];
+            if (ZP) {
+                cmx[c] = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), fmaxf(v[6], v[7]));
+                cmn[c] = min3f(min3f(v[0], v[1], v[2]), min3f(v[3], v[4], v[5]), fminf(v[6], v[7]));
+            } else {
+                cmx[c] = max3f(max3f(fabsf(v[0]), fabsf(v[1]), fabsf(v[2])),
+                               max3f(fabsf(v[3]), fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
             }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            mx = fmaxf(mx, cmx[c]);
+            if (ZP) mn = fminf(mn, cmn[c]);
         }
         u32x4 iv[2][2];             // reciprocal-row halves of two chunks
         auto fetch_inv = [&](int c) {
@@ -375,12 +380,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // on every SIMD one wavefront keeps the matrix core busy while the other uses the VALU.
     // Every wavefront issues stage(jg + 3) [2 transfers] inside its matrix-core half, which also
     // issues C*RBW X loads (the last chunk of group jg, then the other chunks of group jg + 1), XS
-    // of them before the staging.  E(jg + 1) reads the inputs staged in step jg - 2; vector-memory
-    // operations complete in issue order, and after that staging a wavefront has issued the rest
-    // of that half, C*RBW - XS loads, then one more matrix-core half (C*RBW + 2 operations) if it
-    // computes E first in step jg, two if it computes E second.  The compiler's own waits for the
-    // X registers, which cannot see the staging transfers, wait at most for a staging issued one
-    // E half earlier.  In steps 0 and 1 the prologue has already waited for everything.
+    // of them before the staging.  A staged buffer is filled by the transfers of all wavefronts, so
+    // each wavefront waits for its own share of stage(jg + 2), issued in step jg - 1, right before
+    // the barrier that ends step jg; E(jg + 2) reads it in step jg + 1.  Vector-memory operations
+    // complete in issue order, and after that staging a wavefront has issued the rest of that
+    // half (C*RBW - XS loads) and one more matrix-core half (C*RBW + 2 operations).  The
+    // compiler's own waits for the X registers, which cannot see the staging transfers, wait at
+    // most for a staging issued one E half earlier.  The prologue waited for stages 0-2.
     const bool mfma_first = (wave & 4) == 0;
     int sb = 0;   // jg % 3: Stg[sb] held group jg, consumed by E(jg) in the previous step
     for (int jg = 0; jg < n_groups; ++jg) {
@@ -389,13 +395,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int sjg = min(jg + 3, n_groups - 1);
         if (mfma_first) {
             mfma_group(jg, buf, sjg, sb);
-            wait_vmcnt<C * RBW - XS + 2 * (C * RBW + 2)>();
             compute_E(sbn, buf ^ 1);
         } else {
-            wait_vmcnt<C * RBW - XS + C * RBW + 2>();
             compute_E(sbn, buf ^ 1);
             mfma_group(jg, buf, sjg, sb);
         }
+        wait_vmcnt<2 * C * RBW - XS + 2>();
         lds_barrier();
         sb = sbn;
     }
