@@ -161,3 +161,33 @@ def test_scale_table_entry_point():
     A.awq_scale_table(torch.from_numpy(m).cuda(), 21, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), O.scale_table(m, 21))
+
+
+# M = 1 products on wide layers: many K ranges (partials added in a second kernel), a partial
+# last column block, K not a multiple of the groups per workgroup, and each group size.  The
+# packed weights come from the GPU pack of random W with a random scale vector; the reference
+# dequantizes them in float64.
+@pytest.mark.parametrize("K,N,g,zp", [(512, 4096, 128, True), (8192, 4096, 128, True),
+                                      (8832, 4104, 128, True), (2048, 4096, 64, False),
+                                      (1024, 4128, 32, True), (28672, 4096, 128, True)])
+def test_gemv_wide_layers(K, N, g, zp):
+    A = awq()
+    dev = torch.device("cuda:0")
+    log(f"[gemv] K={K} N={N} g={g} zp={zp}")
+    L = I.small(2, K, N, seed=K + N, group_size=g, zero_point=zp)
+    s = torch.from_numpy(I.scale_vector(K, seed=K)).to(dev)
+    W = L.W.to(dev)
+    cfg = A.qconfig(g, zp, 21)
+    codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+    zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+    A.awq_pack(W, s, cfg, codes, scales, zeros)
+    q = A.Quantized(codes, scales, zeros, s, g)
+    Y = gpu_gemm(L.X[:1].contiguous(), q)
+    Yr = O.w4a16_ref(I.bf16_to_f64(L.X[:1]), s.cpu().numpy(), codes.cpu().numpy().view(np.uint32),
+                     scales.cpu().numpy(), zeros.cpu().numpy(), g)
+    err = rel_fro(Y, Yr)
+    log(f"[gemv] K={K} N={N} g={g}: rel Frobenius err {err:.2e}")
+    assert err <= 2e-2
+    Y2 = gpu_gemm(L.X[:1].contiguous(), q)
+    assert np.array_equal(Y, Y2)   # fixed-order reductions

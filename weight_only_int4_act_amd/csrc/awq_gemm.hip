@@ -96,21 +96,30 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
-// HBM-bound: every byte of packed weights is read once.  A wavefront owns 256 output columns and
-// one quantization group (G rows).  Each lane reads 4 adjacent columns x 8 rows of codes with one
-// 16-byte load per code row (a wavefront reads 1 KB of one code row: fully coalesced) and issues
-// all G/8 loads of its group before consuming them.  Nibbles k and k+4 of a code word become two
-// bf16 values 128 + q with one and-or (plus one shift), and v_dot2c_f32_bf16 multiplies them with
-// the pair (x'_k, x'_{k+4}) of activations x' = bf16(x/s) staged in LDS in that pair order.  The
-// offset and the zero point come out once per group: sum (q - z) x' = sum (128 + q) x' -
-// (128 + z) sum x', where sum x' adds the same bf16-rounded values the products used.
-// The 4 wavefronts of a workgroup take 4 consecutive groups and reduce through LDS in a fixed
-// order; workgroups along K write float32 partials with plain stores and a second small kernel
-// adds them in a fixed order and writes the bf16 outputs.  (A last-arriving-workgroup handoff
-// inside one kernel would need device-scope release/acquire, which on this multi-die GPU writes
-// back and invalidates a whole L2 per workgroup.)  No atomics: results are deterministic.
+// HBM-bound: every byte of packed weights is read once.  A workgroup owns 256 output columns and
+// 4*GPW quantization groups (G rows each): wavefront w takes groups 4i + w, i < GPW, of them.  Each
+// lane reads 4 adjacent columns x 8 rows of codes with one 16-byte load per code row (a
+// wavefront reads 1 KB of one code row: fully coalesced); the loads of the next group are issued
+// before the current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values
+// 128 + q with one shift and one and-or, and v_dot2c_f32_bf16 multiplies them with the pair
+// (x'_k, x'_{k+4}) of activations x' = bf16(x/s) staged in LDS in that pair order.  The offset
+// and the zero point come out once per group: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x',
+// where sum x' adds the same bf16-rounded values the products used.  The 4 wavefronts reduce
+// through LDS in a fixed order; workgroups along K write float32 partials with plain stores and a
+// second small kernel adds them in a fixed order and writes the bf16 outputs.  (A
+// last-arriving-workgroup handoff inside one kernel would need device-scope release/acquire,
+// which on this multi-die GPU writes back and invalidates a whole L2 per workgroup.)  No atomics:
+// results are deterministic.
 constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
-constexpr int kGemvWaves = 4;    // groups per workgroup
+constexpr int kGemvWaves = 4;    // wavefronts per workgroup
+constexpr int kGemvGpw = 1;      // groups per wavefront
+
+// (a & b) | c in one instruction (at most one scalar operand: the VOP3 constant-bus limit).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
 
 template <int G>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
@@ -119,66 +128,114 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                                                     const uint8_t* __restrict__ zeros, int K, int N,
                                                     uint16_t* __restrict__ Y, float* __restrict__ part) {
     constexpr int R = G / 8;                     // code rows per group
-    __shared__ uint32_t xpair[kGemvWaves][G / 2]; // code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
-    __shared__ float sxs[kGemvWaves];
+    constexpr int NG = kGemvWaves * kGemvGpw;    // groups per workgroup
+    // x' of the workgroup's groups: group slot i, code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
+    __shared__ uint32_t xpair[NG][G / 2];
+    __shared__ float sxs[NG];
     __shared__ float red[kGemvWaves][kGemvCols];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
     const int n_groups = K / G;
-    const int g = kb * kGemvWaves + wave;
-    const bool gvalid = g < n_groups;
-    const int gg = gvalid ? g : n_groups - 1;
     const int n0 = cb * kGemvCols + lane * 4;
     const bool nvalid = n0 < N;                  // N % 4 == 0
     const int nc = nvalid ? n0 : N - 4;
+    auto group_of = [&](int i) { return kb * NG + kGemvWaves * i + wave; };   // i-th group of this wave
 
-    // issue every code load of the group first (R x 16 bytes per lane in flight)
-    u32x4 cw[R];
-    const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
+    struct Buf {
+        u32x4 cw[R];
+        floatx4 dsc;
+        uint32_t zw;
+    };
+    Buf b0, b1;
+    auto issue = [&](int i, Buf& b) {
+        const int gg = min(group_of(i), n_groups - 1);
+        const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
 #pragma unroll
-    for (int r = 0; r < R; ++r) cw[r] = *(const u32x4*)(cbase + (int64_t)r * N);
-    const floatx4 dsc = *(const floatx4*)(scales + (int64_t)gg * N + nc);
-    const uint32_t zw = *(const uint32_t*)(zeros + (int64_t)gg * N + nc);
-
-    // x' = bf16(x / s) of the group in pair order: lane l < G/2 forms pair l (row l/4, slot l%4)
-    float sx = 0.f;
-    if (lane < G / 2) {
-        const int r = lane >> 2, j = lane & 3;
-        const int k1 = gg * G + 8 * r + j, k2 = k1 + 4;
-        const __bf16 b1 = (__bf16)(bf16_lo((uint32_t)X[k1]) / s[k1]);
-        const __bf16 b2 = (__bf16)(bf16_lo((uint32_t)X[k2]) / s[k2]);
-        sx = (float)b1 + (float)b2;
-        xpair[wave][lane] = (uint32_t)__builtin_bit_cast(unsigned short, b1) |
-                            ((uint32_t)__builtin_bit_cast(unsigned short, b2) << 16);
+        for (int r = 0; r < R; ++r) b.cw[r] = *(const u32x4*)(cbase + (int64_t)r * N);
+        b.dsc = *(const floatx4*)(scales + (int64_t)gg * N + nc);
+        b.zw = *(const uint32_t*)(zeros + (int64_t)gg * N + nc);
+    };
+    // x' of the workgroup's NG groups in pair order: thread t forms pair t % (G/2) of group slot
+    // t / (G/2); the group sums come from a fixed butterfly over the G/2 lanes of a group.  The
+    // activation and scale loads are issued before the code loads (loads complete in order), so
+    // x' is formed while the codes are still in flight.
+    constexpr int XI = (NG * (G / 2) + 255) / 256;   // pairs per thread
+    float xa[XI][2], sa[XI][2];
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+        const int t = 256 * u + (int)threadIdx.x;
+        const int slot = t / (G / 2), l = t % (G / 2);
+        const int gg = min(kb * NG + min(slot, NG - 1), n_groups - 1);
+        const int k1 = gg * G + 8 * (l >> 2) + (l & 3), k2 = k1 + 4;
+        xa[u][0] = bf16_lo((uint32_t)X[k1]);
+        xa[u][1] = bf16_lo((uint32_t)X[k2]);
+        sa[u][0] = s[k1];
+        sa[u][1] = s[k2];
     }
-    sx = wave_sum(sx);
-    if (lane == 0) sxs[wave] = sx;
+    __builtin_amdgcn_sched_barrier(0);   // keep the activation loads ahead of the code loads
+    issue(0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+        const int t = 256 * u + (int)threadIdx.x;
+        const int slot = t / (G / 2), l = t % (G / 2);
+        float sx = 0.f;
+        if (slot < NG) {
+            const __bf16 x1 = (__bf16)(xa[u][0] / sa[u][0]);
+            const __bf16 x2 = (__bf16)(xa[u][1] / sa[u][1]);
+            sx = (float)x1 + (float)x2;
+            xpair[slot][l] = (uint32_t)__builtin_bit_cast(unsigned short, x1) |
+                             ((uint32_t)__builtin_bit_cast(unsigned short, x2) << 16);
+        }
+#pragma unroll
+        for (int o = 1; o < G / 2 && o < 64; o <<= 1) sx += __shfl_xor(sx, o, 64);
+        if (slot < NG && l == 0) sxs[slot] = sx;
+    }
     __syncthreads();
 
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t nib = 0x000F000Fu;
+    const uint32_t bf128 = __builtin_amdgcn_readfirstlane(0x43004300u);
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](int i, const Buf& b) {
+        const int slot = kGemvWaves * i + wave;
+        if (group_of(i) >= n_groups) return;
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        uint32_t xp[4];
+        for (int r = 0; r < R; ++r) {
+            uint32_t xp[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xp[j] = xpair[wave][4 * r + j];   // broadcast reads
+            for (int j = 0; j < 4; ++j) xp[j] = xpair[slot][4 * r + j];   // broadcast reads
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t w = cw[r][c];
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = b.cw[r][c];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t h = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u;   // bf16 (128+q_j, 128+q_{j+4})
-                acc[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
-                                                         __builtin_bit_cast(bf16x2_t, xp[j]), acc[c], false);
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t h = and_or(w >> (4 * j), nib, bf128);   // bf16 (128+q_j, 128+q_{j+4})
+                    d[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
+                                                           __builtin_bit_cast(bf16x2_t, xp[j]), d[c], false);
+                }
             }
         }
-    }
-    const float sxw = sxs[wave];
+        const float sx = sxs[slot];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float z = (float)((zw >> (8 * c)) & 0xFFu);
-        red[wave][lane * 4 + c] = gvalid ? dsc[c] * fmaf(-(128.f + z), sxw, acc[c]) : 0.f;
+        for (int c = 0; c < 4; ++c) {
+            const float z = (float)((b.zw >> (8 * c)) & 0xFFu);
+            acc[c] = fmaf(b.dsc[c], fmaf(-(128.f + z), sx, d[c]), acc[c]);
+        }
+    };
+    // two groups per step, so each buffer keeps a fixed set of registers
+#pragma unroll
+    for (int i = 0; i < kGemvGpw; i += 2) {
+        if (i + 1 < kGemvGpw) issue(i + 1, b1);
+        consume(i, b0);
+        if (i + 1 < kGemvGpw) {
+            if (i + 2 < kGemvGpw) issue(i + 2, b0);
+            consume(i + 1, b1);
+        }
     }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) red[wave][lane * 4 + c] = acc[c];
     __syncthreads();
     const int col = cb * kGemvCols + (int)threadIdx.x;
     const float ps = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
@@ -191,21 +248,33 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     }
 }
 
-// Y[n] = bf16(sum_b part[b][n]) in a fixed order.
+// Y[n] = bf16(sum_b part[b][n]) in a fixed order.  A workgroup takes 32 columns; thread (c, l)
+// adds partials b = l, l + 8, ... of column c (all its loads in flight at once), and the 8 sums of
+// a column are added in lane order through LDS.  Wide enough to keep many loads in flight even for
+// a few thousand columns.
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int nkb, int N,
                                                      uint16_t* __restrict__ Y) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
+    __shared__ float sm[8][32];
+    const int c = threadIdx.x & 31, l = threadIdx.x >> 5;
+    const int n = blockIdx.x * 32 + c;
+    const int nn = n < N ? n : N - 1;
     float t = 0.f;
-    for (int b0 = 0; b0 < nkb; b0 += 8) {   // 8 loads in flight, added in the same fixed order
+    for (int b0 = l; b0 < nkb; b0 += 8 * 8) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = b0 + j < nkb ? part[(int64_t)(b0 + j) * N + n] : 0.f;
+        for (int j = 0; j < 8; ++j) v[j] = b0 + 8 * j < nkb ? part[(int64_t)(b0 + 8 * j) * N + nn] : 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) t += v[j];
     }
-    const __bf16 o = (__bf16)t;
-    Y[n] = __builtin_bit_cast(uint16_t, o);
+    sm[l][c] = t;
+    __syncthreads();
+    if (l == 0 && n < N) {
+        float u = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u += sm[i][c];
+        const __bf16 o = (__bf16)u;
+        Y[n] = __builtin_bit_cast(uint16_t, o);
+    }
 }
 
 namespace {
@@ -225,7 +294,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     if (M == 1) {
         p.variant = 0;
         p.grid_x = (N + kGemvCols - 1) / kGemvCols;
-        p.grid_y = (K / group_size + kGemvWaves - 1) / kGemvWaves;
+        p.grid_y = (K / group_size + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
         p.off_part = 0;
@@ -258,7 +327,7 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint3
             k_w4a16_gemv<128><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.grid_y == 1) return e;
-        k_gemv_reduce<<<(unsigned)((N + 255) / 256), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);
+        k_gemv_reduce<<<(unsigned)((N + 31) / 32), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);
         return hipGetLastError();
     }
     gemm_fn fn = p.variant == 1 ? pick_g<1>(group_size) : pick_g<4>(group_size);

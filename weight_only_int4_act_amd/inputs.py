@@ -102,6 +102,13 @@ def small(T: int, K: int, N: int, seed: int = 0, group_size: int = 128,
     return Layer(f"small_{T}x{K}x{N}", to_bf16(X), to_bf16(W), group_size, zero_point)
 
 
+def scale_vector(K: int, seed: int = 0, sigma: float = 1.0) -> np.ndarray:
+    """A positive float32 per-input-channel scale vector (lognormal draws), standing in for the
+    s* of a search when a product is tested on its own."""
+    rng = np.random.default_rng(seed)
+    return rng.lognormal(0.0, sigma, K).astype(np.float32)
+
+
 def _c1(seed):
     rng = np.random.default_rng(seed)
     W = _normal(rng, (512, 512)) * np.float32(0.02)
