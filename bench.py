@@ -56,17 +56,29 @@ def parse():
     return ap.parse_args()
 
 
+def search_source_digest():
+    """SHA-256 of the search kernel's code (its source file and the device helpers it includes),
+    with `//` comments and blank lines dropped, so that only a change to the code itself makes the
+    recorded counters stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("awq_search.hip", "awq_device.h"):
+        with open(os.path.join(HERE, "weight_only_int4_act_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def search_traffic():
     """HBM-side bytes per search launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-    (scaled by the copy-kernel calibration), or None once the kernel source changed since then."""
-    import hashlib
+    (scaled by the copy-kernel calibration), or None once the kernel code changed since then."""
     prof = os.path.join(HERE, "profiles", "search_c2_hbm_traffic.md")
     try:
         text = open(prof, encoding="utf-8").read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-        src = b"".join(open(os.path.join(HERE, "weight_only_int4_act_amd", "csrc", f), "rb").read()
-                       for f in ("awq_search.hip", "awq_device.h"))
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        if search_source_digest() != rec["source_sha256"]:
             return None
         return float(rec["bytes_per_launch"])
     except (OSError, IndexError, KeyError, ValueError):

@@ -16,9 +16,11 @@
 //     (or max|p|) is an in-register max3/min3 reduction plus two cross-lane steps.  The error
 //     tile E_i = (q*Delta - s*w)/s is rounded to bf16 and written to LDS directly in the
 //     matrix-core operand layout (double buffered, one barrier per group).
-//   * Every wavefront keeps the bf16 X fragments of its rows for the current 32-wide K chunk in
-//     registers (loaded once, prefetched one chunk ahead) and reuses them for all NA alphas:
+//   * Every wavefront keeps the bf16 X fragments of its rows for the current group in registers
+//     (read from a tiled copy of X, one group ahead) and reuses them for all NA alphas:
 //     acc[alpha][row block] += X_chunk . E_alpha_chunk on v_mfma_f32_16x16x32_bf16.
+//   * The inputs of the E computation (float32 W tile, scale and reciprocal rows) reach LDS by
+//     direct global->LDS transfers, three groups in flight.
 //   * Epilogue: sum of squares of the float32 accumulators, reduced in a fixed order to one
 //     float64 partial per (token tile, column tile, alpha).  A second kernel sums the partials
 //     in a fixed order and a third picks the first minimum.
