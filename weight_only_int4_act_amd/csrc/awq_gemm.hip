@@ -15,84 +15,164 @@
 
 namespace awq {
 
-// Workgroup: 4 wavefronts, 64 output columns (16 per wavefront) x 16*MB token rows.
+// (a & b) | c in one instruction (at most one scalar operand: the VOP3 constant-bus limit).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
+
+// ---------------------------------------------------------------- M > 1: matrix-core product
+// Code word (i, n) holds rows 8i + j (j < 8) of column n at bits 4j..4j+3.  One and-or turns
+// nibbles j and j + 4 of a word (shifted right by 4j) into the bf16 pair (128 + q_j, 128 + q_{j+4}),
+// so a word becomes a matrix-core B operand whose 8 k slots are rows (0, 4, 1, 5, 2, 6, 3, 7) of the
+// word.  The A operand holds x' = bf16(x / s) in the same slot order, so the product sums
+// x'_k (128 + q_k); the offset and the zero point leave once per group and column:
+//   sum_k x'_k (q_k - z) = sum_k x'_k (128 + q_k) - (128 + z) sum_k x'_k,
+// where sum_k x'_k adds the same bf16-rounded values, and the accumulator of a group starts at
+// -(128 + z) sum x' so that the products complete it.
+
+// x' = bf16(x / s) in A-operand order and its group sums.  Thread t owns row m = t / (K/8) and the
+// 8 channels 8*kb .. 8*kb+7 (kb = t % (K/8)); it writes them as the 16 bytes lane 16*(kb%4) + m%16
+// of fragment (m/16, kb/4) feeds to the matrix core:
+//   Xp[((m/16) * (K/32) + kb/4) * 64 + 16*(kb%4) + m%16] = pairs (x'_{8kb+j}, x'_{8kb+j+4}), j < 4.
+// The G/8 consecutive threads of one group add their sums with a fixed butterfly; the first writes
+// Sg[g * mpad + m].  Rows m in [M, mpad) are zero.
+template <int G>
+__global__ __launch_bounds__(256) void k_prep_x(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                const float* __restrict__ s, int64_t mpad, u32x4* __restrict__ Xp,
+                                                float* __restrict__ Sg) {
+    const int64_t kbs = K / 8;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = t < mpad * kbs;            // the grid is rounded up to whole workgroups
+    const int64_t tt = live ? t : 0;
+    const int64_t m = tt / kbs, kb = tt % kbs;
+    float x[8];
+    if (live && m < M) {
+        const u32x4 xv = *(const u32x4*)(X + m * K + 8 * kb);
+        const floatx4 s0 = *(const floatx4*)(s + 8 * kb);
+        const floatx4 s1 = *(const floatx4*)(s + 8 * kb + 4);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float sl = h < 2 ? s0[2 * h] : s1[2 * h - 4];
+            const float sh = h < 2 ? s0[2 * h + 1] : s1[2 * h - 3];
+            x[2 * h] = (float)(__bf16)(bf16_lo(xv[h]) / sl);
+            x[2 * h + 1] = (float)(__bf16)(bf16_hi(xv[h]) / sh);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    float sx = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+#pragma unroll
+    for (int o = 1; o < G / 8; o <<= 1) sx += __shfl_xor(sx, o, 64);
+    if (!live) return;
+    Xp[((m >> 4) * (K / 32) + (kb >> 2)) * 64 + 16 * (kb & 3) + (m & 15)] =
+        u32x4{pack_bf16x2(x[0], x[4]), pack_bf16x2(x[1], x[5]), pack_bf16x2(x[2], x[6]), pack_bf16x2(x[3], x[7])};
+    if (kb % (G / 8) == 0) Sg[(kb / (G / 8)) * mpad + m] = sx;
+}
+
+// Workgroup: 4 wavefronts over the same 16*MB rows x 64 columns, splitting the workgroup's groups
+// of K between them (wavefront w takes groups gb + w, gb + w + 4, ...); a fixed-order sum through
+// LDS joins them.  Lane (r16, q) owns the 4 adjacent columns n0 = 64*bx + 4*r16 .. n0 + 3 (one
+// 16-byte code load per code row) and uses column n0 + j as column r16 of its j-th 16-column
+// matrix-core tile; its accumulators hold rows 4q .. 4q+3 of each 16-row block.  With ksplit > 1
+// the workgroups along K write float32 partials, added in a fixed order by k_gemv_reduce.
 template <int G, int MB>
-__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__ X, int64_t M,
-                                                    const float* __restrict__ s,
-                                                    const uint32_t* __restrict__ codes,
-                                                    const float* __restrict__ scales,
-                                                    const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
-                                                    uint16_t* __restrict__ Y) {
+__global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ Xp, const float* __restrict__ Sg,
+                                                   int64_t mpad, int64_t M, const uint32_t* __restrict__ codes,
+                                                   const float* __restrict__ scales,
+                                                   const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
+                                                   uint16_t* __restrict__ Y, float* __restrict__ part) {
     constexpr int C = G / 32;
+    __shared__ floatx4 red[3][MB][4][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = lane >> 4, r16 = lane & 15;
-    const int64_t n = (int64_t)blockIdx.x * 64 + wave * 16 + r16;
-    const bool nvalid = n < N;
-    const int64_t nc = nvalid ? n : N - 1;
-    const int64_t m0 = (int64_t)blockIdx.y * 16 * MB;
-    const int64_t n_groups = K / G;
+    const int64_t n0 = (int64_t)blockIdx.x * 64 + 4 * r16;
+    const bool nvalid = n0 < N;                  // N % 8 == 0: n0 < N implies n0 + 3 < N
+    const int64_t nc = nvalid ? n0 : 0;
+    const int64_t R0 = (int64_t)blockIdx.y * MB;  // first 16-row block
+    const int64_t n_groups = K / G, kchunks = K / 32;
+    const int64_t gpk = (n_groups + gridDim.z - 1) / gridDim.z;
+    const int64_t gb = (int64_t)blockIdx.z * gpk;
+    const int64_t ge = min(gb + gpk, n_groups);
 
-    const uint16_t* xr[MB];
-    bool mvalid[MB];
+    // the nibble mask in a vector register and the bf16 bias in a scalar one, so that the compiler
+    // can form each operand pair with one v_and_or_b32 (one scalar operand per VOP3)
+    uint32_t nib;
+    asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(nib));
+    const uint32_t bf128 = __builtin_amdgcn_readfirstlane(0x43004300u);
+    floatx4 acc[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = m0 + 16 * mb + r16;
-        mvalid[mb] = m < M;
-        xr[mb] = X + (mvalid[mb] ? m : M - 1) * K + 8 * q;
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    floatx4 acc[MB];
+    for (int64_t g = gb + wave; g < ge; g += 4) {
+        const floatx4 dsc = *(const floatx4*)(scales + g * N + nc);
+        const uint32_t zw = *(const uint32_t*)(zeros + g * N + nc);
+        floatx4 accg[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t jg = 0; jg < n_groups; ++jg) {
-        const float d = scales[jg * N + nc];
-        const float z = (float)zeros[jg * N + nc];
-        floatx4 accg[MB];
+        for (int mb = 0; mb < MB; ++mb) {
+            const floatx4 sv = *(const floatx4*)(Sg + g * mpad + (R0 + mb) * 16 + 4 * q);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) accg[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) {
+                const float off = -(128.f + (float)((zw >> (8 * j)) & 0xFFu));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accg[mb][j][i] = off * sv[i];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int64_t k0 = jg * G + 32 * c + 8 * q;
-            const uint32_t word = nvalid ? codes[(k0 >> 3) * N + nc] : 0u;
-            u32x4 bw;
+            const u32x4 cw = *(const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc);
+            u32x4 a[MB];
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float lo = nvalid ? (float)((word >> (8 * h)) & 0xF) - z : 0.f;
-                const float hi = nvalid ? (float)((word >> (8 * h + 4)) & 0xF) - z : 0.f;
-                bw[h] = pack_bf16x2(lo, hi);
-            }
-            const floatx4 s0 = *(const floatx4*)(s + k0);
-            const floatx4 s1 = *(const floatx4*)(s + k0 + 4);
+            for (int mb = 0; mb < MB; ++mb) a[mb] = Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const u32x4 xv = *(const u32x4*)(xr[mb] + jg * G + 32 * c);
-                u32x4 av;
+            for (int j = 0; j < 4; ++j) {
+                // plain C (the compiler emits v_and_or_b32): these values feed the matrix core
+                // directly, and only code the compiler sees gets its VALU -> MFMA wait states
+                const u32x4 b = u32x4{(cw[j] & nib) | bf128, ((cw[j] >> 4) & nib) | bf128,
+                                      ((cw[j] >> 8) & nib) | bf128, ((cw[j] >> 12) & nib) | bf128};
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float sl = h < 2 ? s0[2 * h] : s1[2 * h - 4];
-                    const float sh = h < 2 ? s0[2 * h + 1] : s1[2 * h - 3];
-                    av[h] = mvalid[mb] ? pack_bf16x2(bf16_lo(xv[h]) / sl, bf16_hi(xv[h]) / sh) : 0u;
-                }
-                accg[mb] = mfma16x16x32(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bw), accg[mb]);
+                for (int mb = 0; mb < MB; ++mb)
+                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b),
+                                               accg[mb][j]);
             }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(d, accg[mb][i], acc[mb][i]);
-    }
-    if (!nvalid) return;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+                for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(dsc[j], accg[mb][j][i], acc[mb][j][i]);
+    }
+
+    if (wave > 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wave - 1][mb][j][lane] = acc[mb][j];
+    }
+    __syncthreads();
+    if (wave > 0 || !nvalid) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        floatx4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = ((acc[mb][j] + red[0][mb][j][lane]) + red[1][mb][j][lane]) + red[2][mb][j][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t m = m0 + 16 * mb + 4 * q + i;
-            if (m < M) {
-                const __bf16 v = (__bf16)acc[mb][i];
-                Y[m * N + n] = __builtin_bit_cast(uint16_t, v);
+            const int64_t m = (R0 + mb) * 16 + 4 * q + i;
+            if (m >= M) continue;
+            if (gridDim.z == 1) {
+                const uint32_t lo = pack_bf16x2(v[0][i], v[1][i]), hi = pack_bf16x2(v[2][i], v[3][i]);
+                *(uint2*)(Y + m * N + n0) = uint2{lo, hi};
+            } else {
+                *(floatx4*)(part + ((int64_t)blockIdx.z * M + m) * N + n0) = floatx4{v[0][i], v[1][i], v[2][i], v[3][i]};
             }
         }
+    }
 }
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
@@ -113,13 +193,6 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
 constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
 constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 constexpr int kGemvGpw = 1;      // groups per wavefront
-
-// (a & b) | c in one instruction (at most one scalar operand: the VOP3 constant-bus limit).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
-    return r;
-}
 
 template <int G>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
@@ -278,38 +351,65 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
 }
 
 namespace {
-typedef void (*gemm_fn)(const uint16_t*, int64_t, const float*, const uint32_t*, const float*, const uint8_t*,
-                        int64_t, int64_t, uint16_t*);
-template <int MB>
-gemm_fn pick_g(int g) {
-    if (g == 32) return k_w4a16_mfma<32, MB>;
-    if (g == 64) return k_w4a16_mfma<64, MB>;
-    if (g == 128) return k_w4a16_mfma<128, MB>;
-    return nullptr;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int G>
+hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes, const float* scales,
+                      const uint8_t* zeros, int64_t K, int64_t N, uint16_t* Y, void* ws, const GemmPlan& p,
+                      hipStream_t st) {
+    char* base = (char*)ws;
+    u32x4* Xp = (u32x4*)(base + p.off_xp);
+    float* Sg = (float*)(base + p.off_sg);
+    float* part = (float*)(base + p.off_part);
+    const int64_t threads = p.mpad * (K / 8);
+    k_prep_x<G><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(X, M, K, s, p.mpad, Xp, Sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
+    if (p.variant == 1)
+        k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+    else if (p.variant == 2)
+        k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+    else
+        k_w4a16_mma<G, 4><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.ksplit == 1) return e;
+    k_gemv_reduce<<<(unsigned)((M * N + 31) / 32), 256, 0, st>>>(part, p.ksplit, (int)(M * N), Y);
+    return hipGetLastError();
 }
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     GemmPlan p{};
+    const int64_t n_groups = K / group_size;
     if (M == 1) {
         p.variant = 0;
         p.grid_x = (N + kGemvCols - 1) / kGemvCols;
-        p.grid_y = (K / group_size + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
+        p.grid_y = (n_groups + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
-        p.off_part = 0;
-        p.off_cnt = 0;
+        p.mpad = 1;
         p.ws_bytes = p.grid_y > 1 ? (size_t)p.grid_y * N * sizeof(float) : 0;
         return p;
     }
-    p.variant = M <= 16 ? 1 : 4;
+    // 16-row blocks per wavefront: as many as the rows need, up to 4 (64 rows x 64 columns)
+    p.variant = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    const int64_t rows = 16 * p.variant;
+    p.mpad = (M + rows - 1) / rows * rows;
     p.grid_x = (N + 63) / 64;
-    p.grid_y = (M + 16 * p.variant - 1) / (16 * p.variant);
-    p.grid_z = 1;
-    p.ksplit = 1;
-    p.off_part = 0;
-    p.off_cnt = 0;
-    p.ws_bytes = 0;
+    p.grid_y = p.mpad / rows;
+    // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping at least
+    // one group per wavefront and the partials' index range within int
+    const int64_t tiles = p.grid_x * p.grid_y;
+    int64_t ks = 1;
+    while (tiles * ks < 512 && 2 * ks * 4 <= n_groups && 2 * ks * M * N < ((int64_t)1 << 31)) ks *= 2;
+    p.grid_z = ks;
+    p.ksplit = (int)ks;
+    size_t off = 0;
+    p.off_part = off; off = align256(off + (ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0));
+    p.off_xp = off;   off = align256(off + (size_t)p.mpad * K * sizeof(uint16_t));
+    p.off_sg = off;   off = align256(off + (size_t)n_groups * p.mpad * sizeof(float));
+    p.ws_bytes = off;
     return p;
 }
 
@@ -330,11 +430,10 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint3
         k_gemv_reduce<<<(unsigned)((N + 31) / 32), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);
         return hipGetLastError();
     }
-    gemm_fn fn = p.variant == 1 ? pick_g<1>(group_size) : pick_g<4>(group_size);
-    if (!fn) return hipErrorInvalidValue;
-    dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
-    fn<<<grid, 256, 0, st>>>(X, M, s, codes, scales, zeros, K, N, Y);
-    return hipGetLastError();
+    if (group_size == 32) return launch_mma<32>(X, M, s, codes, scales, zeros, K, N, Y, ws, p, st);
+    if (group_size == 64) return launch_mma<64>(X, M, s, codes, scales, zeros, K, N, Y, ws, p, st);
+    if (group_size == 128) return launch_mma<128>(X, M, s, codes, scales, zeros, K, N, Y, ws, p, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace awq

@@ -46,10 +46,12 @@ hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, 
 
 // ---- a6: W4A16 product
 struct GemmPlan {
-    int variant;
+    int variant;             // 0: M = 1 GEMV; else row blocks of 16 per wavefront (1, 2 or 4)
     int64_t grid_x, grid_y, grid_z;
-    int ksplit;
-    size_t off_part, off_cnt, ws_bytes;
+    int ksplit;              // workgroups along K (float32 partials added by a second kernel)
+    int64_t mpad;            // M rounded up to the workgroup's row tile
+    // workspace layout (byte offsets): split-K partials, x' in fragment order, group sums of x'
+    size_t off_part, off_xp, off_sg, ws_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size);
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes,
