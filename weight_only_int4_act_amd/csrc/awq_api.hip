@@ -73,7 +73,11 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
         return AWQ_ERR_INVALID_ARG;
     const awq::SearchPlan p = awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid);
     // tile counts and the 16-byte index into the tiled copy of X are 32-bit in the kernel
-    if (p.tiles > kIntMax || p.tb * p.bm * K / 8 > kIntMax) return AWQ_ERR_INVALID_ARG;
+    // the kernel addresses the staged inputs (scale table, reciprocals, W tiles) and one token tile
+    // of tiled X through buffer resources with 32-bit byte offsets
+    if (p.tiles > kIntMax || p.tb * p.bm * K / 8 > kIntMax || (int64_t)(p.off_xt - p.off_s) > (int64_t)0xffffffff ||
+        (int64_t)p.bm * K * 2 > kIntMax)
+        return AWQ_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs, p,

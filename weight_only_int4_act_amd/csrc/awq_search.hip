@@ -105,20 +105,46 @@ __device__ __forceinline__ float min3f(float a, float b, float c) {
     asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
 }
-// Reduction over the four lanes l, l^16, l^32, l^48 (the four quads of one column) with the
-// gfx950 lane-swap instructions: each returns both halves of the exchange, which are combined
-// symmetrically, so the result is the same in every one of the four lanes.
+// max(-a, -b, -c) = -min(a, b, c), with the negations as free source modifiers.
+__device__ __forceinline__ float nmax3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, -%1, -%2, -%3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float nmaxf(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, -%1, -%2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// max of two values that come out of lane swaps as raw bits (fmaxf would first canonicalize both).
+__device__ __forceinline__ float maxraw(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four quads of one column) with the
+// gfx950 lane-swap instructions.  v_permlane32_swap exchanges the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second; v_permlane16_swap exchanges the odd 16-lane rows
+// of its first operand with the even rows of its second.
+// quad_max: every lane ends with the maximum of v over its column.
 __device__ __forceinline__ float quad_max(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = maxraw(a[0], a[1]);
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return maxraw(b[0], b[1]);
 }
-__device__ __forceinline__ float quad_min(float v) {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// quad_max2: both maxima of (x, y) over the column in one network.  The first swap pairs x of
+// lanes l, l+32 in the lower half and y of lanes l-32, l in the upper half; after the row swap the
+// lower half holds the column maximum of x and the upper half that of y; the last swap hands each
+// lane both.
+__device__ __forceinline__ void quad_max2(float& x, float& y) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float t = maxraw(a[0], a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    const float u = maxraw(b[0], b[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    x = __uint_as_float(c[0]);
+    y = __uint_as_float(c[1]);
 }
 
 // LDS-only workgroup barrier.  Every cross-wavefront exchange in the search goes through ds_write
@@ -127,23 +153,37 @@ __device__ __forceinline__ float quad_min(float v) {
 // with counted vmcnt waits at their use, so the barrier must not drain them.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Direct global -> LDS transfer of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
-// land at LDS address `lds + 16*l`.  Issued from inline asm so that the compiler does not track
-// it: every wait for these transfers is an explicit, counted s_waitcnt vmcnt(N) (vmcnt counts
-// vector-memory operations that complete in issue order).  M0 carries the LDS base; it is saved
-// and restored around the transfer, and one wait state separates the M0 write from its use.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+// Buffer resource (V#) of a raw byte range: base address, no stride, num_records bytes (accesses at
+// or beyond it return zero), and the gfx9 word 3 for untyped 32-bit data.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 byte_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, 0x00020000};
+}
+
+// Direct buffer -> LDS transfer of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l's bytes
+// (at byte offset voff of the resource) land at LDS address `lds + 16*l`.  Issued from inline asm
+// so that the compiler does not track it: every wait for these transfers is an explicit, counted
+// s_waitcnt vmcnt(N) (vmcnt counts vector-memory operations that complete in issue order).  M0
+// carries the LDS base; it is saved and restored around the transfer, and one wait state
+// separates the M0 write from its use.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "memory");
 }
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -153,7 +193,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int G, int NA, int RBW, int NW, bool ZP>
 __global__ __launch_bounds__(NW * 64, 1) void k_search(
     const u32x4* __restrict__ Xt, int T, int K, const floatx4* __restrict__ Wt, int NB,
-    const float* __restrict__ s_tab, const float* __restrict__ inv_tab, int n_grid, int n_asplit,
+    const float* __restrict__ s_tab, const float* __restrict__ inv_tab, uint32_t stage_bytes, int n_grid, int n_asplit,
     int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
     constexpr int C = G / 32;            // K chunks per group
     constexpr int BM = NW * RBW * 16;    // token rows per workgroup
@@ -177,10 +217,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 
     // E tiles (bf16, B-operand layout), double buffered over groups.
     __shared__ u32x4 Es[2][NA][C][64];
-    // Staged inputs of the E computation of one group, triple buffered (group g in Stg[g % 3]): the
+    // Staged inputs of the E computation of one group, four groups deep (group g in Stg[g % 4]): the
     // W tile (float32, in B-operand order), then NA scale rows, then NA reciprocal rows (16-byte
     // entries).
-    __shared__ u32x4 Stg[3][NSTGP];
+    __shared__ u32x4 Stg[4][NSTGP];
     __shared__ double red[NW][NA];
 
     floatx4 acc[NA][RBW];
@@ -193,20 +233,27 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // registers and loaded one group ahead: once the matrix-core work of chunk c of group jg has
     // been issued, the same fragments receive chunk c of group jg + 1.  A load therefore has a whole
     // group step to arrive.  Each load is one contiguous 1 KB block of the tiled X.
-    int xoff[RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) xoff[rb] = (tb * (BM / 16) + wave * RBW + rb) * kchunks * 64 + lane;
+    // The token tile's fragments form one contiguous range of (BM/16) * kchunks KB; a load takes
+    // this lane's byte offset in a vector register and the row block and chunk as a scalar offset.
+    const auto xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + (int64_t)tb * (BM / 16) * kchunks * 64), 0,
+                                                         (BM / 16) * kchunks * 1024, 0x00020000);
+    const uint32_t xvoff = ((uint32_t)(wave * RBW) * kchunks * 64 + lane) * 16;
     u32x4 xr[C][RBW];
     auto load_X = [&](int jg, int c) {
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) xr[c][rb] = Xt[xoff[rb] + (jg * C + c) * 64];
+        for (int rb = 0; rb < RBW; ++rb)
+            xr[c][rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      xrsrc, xvoff, (rb * kchunks + jg * C + c) * 1024, 0));
     };
 
     // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
     // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  The
     // padding entries re-read the last valid entry.
-    const char* stg_src[2];
-    int64_t stg_step[2];
+    // The scale table, its reciprocals and the W tiles lie in one range of the workspace that
+    // starts at s_tab (stage_bytes long, checked below 4 GB by the host); a transfer's source is a
+    // byte offset in it that advances by a fixed step per group.
+    const i32x4 srsrc = byte_rsrc(s_tab, stage_bytes);
+    uint32_t stg_off[2], stg_step[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
@@ -214,20 +261,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int which = es >= NSE;                     // 0: scale row, 1: reciprocal row
         const int idx = es - which * NSE;
         const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
+        const char* src;
         if (e < NWE) {
-            stg_src[r] = (const char*)(Wt + (int64_t)nb * kchunks * 128 + e);
-            stg_step[r] = (int64_t)C * 128 * sizeof(floatx4);
+            src = (const char*)(Wt + (int64_t)nb * kchunks * 128 + e);
+            stg_step[r] = (uint32_t)(C * 128 * sizeof(floatx4));
         } else {
-            stg_src[r] = (const char*)((which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + off);
-            stg_step[r] = (int64_t)G * sizeof(float);
+            src = (const char*)((which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + off);
+            stg_step[r] = (uint32_t)(G * sizeof(float));
         }
+        stg_off[r] = (uint32_t)(src - (const char*)s_tab);
     }
     const uint32_t stg_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&Stg[0][0]) +
                              (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
     auto stage = [&](int jg, int buf) {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
-            dma16(stg_src[r] + jg * stg_step[r], stg_lds + (uint32_t)(buf * NSTGP + NW * 64 * r) * 16);
+            dma16(srsrc, stg_off[r] + (uint32_t)jg * stg_step[r], stg_lds + (uint32_t)(buf * NSTGP + NW * 64 * r) * 16);
     };
 
     // ---- E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].
@@ -244,20 +293,26 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // The staged inputs are read two chunks ahead of their use (the W tile and scale rows in the
     // range pass, the reciprocal rows in the quantization pass), so that LDS latency overlaps the
     // arithmetic of the previous chunk.
-    auto compute_E = [&](int ibuf, int ebuf) {
+    const int srow = NWE + (slot * G) / 4;   // this slot's scale row in a staging buffer
+    u32x4 in[2][4];                          // W halves and scale halves of two chunks
+    auto fetch_in = [&](int ibuf, int c) {
         const u32x4* st = &Stg[ibuf][0];
-        const int srow = NWE + (slot * G) / 4;   // this slot's scale row
+        in[c & 1][0] = st[c * 128 + lane];
+        in[c & 1][1] = st[c * 128 + 64 + lane];
+        in[c & 1][2] = st[srow + kmap<G>(c, q) / 4];
+        in[c & 1][3] = st[srow + kmap<G>(c, q) / 4 + 1];
+    };
+    // The first chunk's inputs are issued ahead of compute_E by the wavefronts whose matrix-core
+    // half comes first (inside its last chunk); compute_E issues the rest, two chunks ahead.
+    auto prefetch_E = [&](int ibuf) { fetch_in(ibuf, 0); };
+    auto compute_E = [&](int ibuf, int ebuf, bool prefetched) {
+        const u32x4* st = &Stg[ibuf][0];
         float pk[C * 8];
-        float mx = 0.f, mn = 0.f;   // ZP: the group range always includes 0; else mx = max|p|
-        u32x4 in[2][4];             // W halves and scale halves of two chunks
-        auto fetch_in = [&](int c) {
-            in[c & 1][0] = st[c * 128 + lane];
-            in[c & 1][1] = st[c * 128 + 64 + lane];
-            in[c & 1][2] = st[srow + kmap<G>(c, q) / 4];
-            in[c & 1][3] = st[srow + kmap<G>(c, q) / 4 + 1];
-        };
-        fetch_in(0);
-        if constexpr (C > 1) fetch_in(1);
+        // ZP: mx = max(p, 0) and nmn = -min(p, 0) (the group range always includes 0); else
+        // mx = max |p|
+        float mx = 0.f, nmn = 0.f;
+        if (!prefetched) fetch_in(ibuf, 0);
+        if constexpr (C > 1) fetch_in(ibuf, 1);
         float cmx[C], cmn[C];       // per-chunk range, combined below as a tree
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -270,11 +325,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                 pk[c * 8 + j] = s0[j] * w0[j];
                 pk[c * 8 + 4 + j] = s1[j] * w1[j];
             }
-            if (c + 2 < C) fetch_in(c + 2);
+            if (c + 2 < C) fetch_in(ibuf, c + 2);
             const float* v = &pk[c * 8];
             if (ZP) {
                 cmx[c] = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), fmaxf(v[6], v[7]));
-                cmn[c] = min3f(min3f(v[0], v[1], v[2]), min3f(v[3], v[4], v[5]), fminf(v[6], v[7]));
+                cmn[c] = max3f(nmax3f(v[0], v[1], v[2]), nmax3f(v[3], v[4], v[5]), nmaxf(v[6], v[7]));
             } else {
                 cmx[c] = max3f(max3f(fabsf(v[0]), fabsf(v[1]), fabsf(v[2])),
                                max3f(fabsf(v[3]), fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
@@ -283,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             mx = fmaxf(mx, cmx[c]);
-            if (ZP) mn = fminf(mn, cmn[c]);
+            if (ZP) nmn = fmaxf(nmn, cmn[c]);
         }
         u32x4 iv[2][2];             // reciprocal-row halves of two chunks
         auto fetch_inv = [&](int c) {
@@ -294,14 +349,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         if constexpr (C > 1) fetch_inv(1);
         float d;
         if (ZP) {
-            mx = quad_max(mx);
-            mn = quad_min(mn);
-            d = (mx - mn) * (1.0f / 15.0f);
+            quad_max2(mx, nmn);
+            d = (mx + nmn) * (1.0f / 15.0f);
         } else {
             mx = quad_max(mx);
             d = mx * (1.0f / 7.0f);
         }
-        d = d == 0.f ? 1.f : d;
+        // an all-zero group has d = 0 and every p = 0, so any finite reciprocal gives e = 0;
+        // below FLT_MIN the step only meets values whose squares vanish in the loss
+        d = fmaxf(d, 1.17549435e-38f);
         const float rd = __builtin_amdgcn_rcpf(d);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -332,7 +388,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // their issue cost hides behind the matrix work; XS = X loads of the half issued before them.
     constexpr int SC = C >= 4 ? 1 : 0;
     constexpr int XS = (C > 1 ? RBW : 0) + (SC + 1) * RBW;
-    auto mfma_group = [&](int jg, int buf, int sjg, int sbuf) {
+    // PRE: after the products of alpha NA-2 in the last chunk (when the other alphas' E fragments
+    // are dead), issue the LDS reads of the first inputs of an E computation (staged in Stg[pbuf]).
+    auto mfma_group = [&](auto pre_tag, int jg, int buf, int sjg, int sbuf, int pbuf) {
+        constexpr bool PRE = decltype(pre_tag)::value;
+        constexpr int PA = NA > 2 ? NA - 2 : 0;
         const int jn = min(jg + 1, n_groups - 1);
         if constexpr (C > 1) load_X(jg, C - 1);
         u32x4 B[NA];
@@ -349,6 +409,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                     acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, xr[c][rb]), __builtin_bit_cast(bf16x8, B[a]),
                                               acc[a][rb]);
                 if (c + 1 < C) B[a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
+                if (PRE && c == C - 1 && a == PA) prefetch_E(pbuf);
             }
             if (c < CL) load_X(jn, c);
             // issue order inside the chunk: per alpha, its RBW products then the next chunk's E
@@ -357,6 +418,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             for (int a = 0; a < NA; ++a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, RBW, 0);   // MFMA
                 if (c + 1 < C) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                if (PRE && c == C - 1 && a == PA)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
             }
             if (c < CL) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
             __builtin_amdgcn_sched_barrier(0);
@@ -364,15 +427,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         }
     };
 
-    // ---- prologue: X of group 0 in registers, inputs of groups 0-2 staged, E(0) computed.
+    // ---- prologue: X of group 0 in registers, inputs of groups 0-3 staged, E(0) computed.
 #pragma unroll
     for (int c = 0; c < CL; ++c) load_X(0, c);
-    stage(0, 0);
-    stage(min(1, n_groups - 1), 1);
-    stage(min(2, n_groups - 1), 2);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) stage(min(g, n_groups - 1), g);
     wait_vmcnt<0>();
     lds_barrier();
-    compute_E(0, 0);
+    compute_E(0, 0, false);
     lds_barrier();
 
     // Main loop.  The two wavefronts that share a SIMD (w and w + 4) run the two halves of a
@@ -380,31 +442,37 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // then compute their E(jg+1) tile; wavefronts 4-7 compute E(jg+1) first and then issue their
     // matrix-core work.  Both halves only read E(jg) and write E(jg+1), so the order is free, and
     // on every SIMD one wavefront keeps the matrix core busy while the other uses the VALU.
-    // Every wavefront issues stage(jg + 3) [2 transfers] inside its matrix-core half, which also
+    // Inside its matrix-core half every wavefront also reads the first inputs of the next E tile it
+    // computes: wavefronts 0-3 those of E(jg+1) (in Stg[(jg+1) % 4]) for the E half that follows,
+    // wavefronts 4-7 those of E(jg+2) (in Stg[(jg+2) % 4]) for the start of the next step, so no
+    // E half begins with an LDS wait.
+    // Every wavefront issues stage(jg + 4) [2 transfers] inside its matrix-core half, which also
     // issues C*RBW X loads (the last chunk of group jg, then the other chunks of group jg + 1), XS
     // of them before the staging.  A staged buffer is filled by the transfers of all wavefronts, so
-    // each wavefront waits for its own share of stage(jg + 2), issued in step jg - 1, right before
-    // the barrier that ends step jg; E(jg + 2) reads it in step jg + 1.  Vector-memory operations
-    // complete in issue order, and after that staging a wavefront has issued the rest of that
-    // half (C*RBW - XS loads) and one more matrix-core half (C*RBW + 2 operations).  The
-    // compiler's own waits for the X registers, which cannot see the staging transfers, wait at
-    // most for a staging issued one E half earlier.  The prologue waited for stages 0-2.
+    // each wavefront waits for its own share of stage(jg + 3), issued in step jg - 1, right before
+    // the barrier that ends step jg; it is read from step jg + 1 on (wavefronts 4-7 read the first
+    // inputs of E(jg + 3) at the end of step jg + 1).  Vector-memory operations complete in issue
+    // order, and after that staging a wavefront has issued the rest of that half (C*RBW - XS loads)
+    // and one more matrix-core half (C*RBW + 2 operations).  The compiler's own waits for the X
+    // registers, which cannot see the staging transfers, wait at most for a staging issued one E
+    // half earlier.  The prologue waited for stages 0-3.
     const bool mfma_first = (wave & 4) == 0;
-    int sb = 0;   // jg % 3: Stg[sb] held group jg, consumed by E(jg) in the previous step
+    if (!mfma_first) prefetch_E(min(1, n_groups - 1) & 3);
     for (int jg = 0; jg < n_groups; ++jg) {
         const int buf = jg & 1;
-        const int sbn = sb == 2 ? 0 : sb + 1;   // (jg + 1) % 3
-        const int sjg = min(jg + 3, n_groups - 1);
+        const int sb = jg & 3;                  // held group jg (consumed by E(jg)); refilled with jg + 4
+        const int sbn = (jg + 1) & 3;           // group jg + 1
+        const int sbn2 = (jg + 2) & 3;          // group jg + 2
+        const int sjg = min(jg + 4, n_groups - 1);
         if (mfma_first) {
-            mfma_group(jg, buf, sjg, sb);
-            compute_E(sbn, buf ^ 1);
+            mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn);
+            compute_E(sbn, buf ^ 1, true);
         } else {
-            compute_E(sbn, buf ^ 1);
-            mfma_group(jg, buf, sjg, sb);
+            compute_E(sbn, buf ^ 1, true);
+            mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn2);
         }
         wait_vmcnt<2 * C * RBW - XS + 2>();
         lds_barrier();
-        sb = sbn;
     }
     // drain the trailing (redundant) transfers before the LDS is reused or released
     wait_vmcnt<0>();
@@ -481,8 +549,8 @@ namespace {
 constexpr int kNA = 7, kRBW = 4, kNW = 8;
 constexpr int kBM = kNW * kRBW * 16;
 
-typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, int,
-                          int, int, int, double*);
+typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, uint32_t,
+                          int, int, int, int, double*);
 
 search_fn pick(int g, int zp) {
     if (zp) {
@@ -551,8 +619,9 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     if ((e = hipGetLastError()) != hipSuccess) return e;
     search_fn fn = pick(p.group_size, p.zero_point);
     if (!fn) return hipErrorInvalidValue;
-    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, p.n_grid,
-                                             p.n_asplit, (int)p.tiles, (int)p.tiles_per_xcd, part);
+    const uint32_t stage_bytes = (uint32_t)(p.off_xt - p.off_s);   // scale table, reciprocals, W tiles
+    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, stage_bytes,
+                                             p.n_grid, p.n_asplit, (int)p.tiles, (int)p.tiles_per_xcd, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_reduce_losses<<<(unsigned)p.n_grid, 256, 0, st>>>(part, p.tb * p.nb, p.n_grid, losses);
     if ((e = hipGetLastError()) != hipSuccess) return e;
