@@ -9,7 +9,7 @@ Bars:
   * search: every L(alpha) within 1e-2 relative of the oracle; the chosen alpha's oracle loss
     within 1e-2 of the oracle minimum; s_best equal to the oracle's scale row of that alpha;
   * W4A16 product: relative Frobenius error <= 2e-2 against the fp64 reference.
-Shapes span several tiles with ragged tails in T (token tiles of 512 rows) and N (column
+Shapes span several tiles with ragged tails in T (token tiles of 512 or 640 rows) and N (column
 tiles of 16), both quantizer modes, all supported group sizes and non-default grids.
 """
 import numpy as np
@@ -33,6 +33,9 @@ CASES = {
     "g32_grid11": (100, 192, 24, 32, True, 11, 3),
     "grid2_minK": (64, 128, 16, 128, True, 2, 4),
     "sym128_multi": (700, 512, 72, 128, False, 21, 5),
+    # token counts for which the search takes 640-row tiles (two tiles, the second ragged)
+    "rows640_zp128": (1250, 384, 40, 128, True, 21, 6),
+    "rows640_zp32": (1270, 256, 24, 32, True, 21, 7),
 }
 
 _cache = {}

@@ -25,7 +25,7 @@ hipError_t launch_scale_table(const float* mean_abs, int64_t K, int n_grid, floa
 // ---- a3/a4: search
 struct SearchPlan {
     int group_size, n_grid, zero_point;
-    int variant;             // kernel instantiation (see awq_search.hip)
+    int variant;             // row blocks of 16 tokens per wavefront (4 or 5)
     int na;                  // alpha slots per workgroup
     int bm;                  // token rows per workgroup
     int n_asplit;            // alpha slices

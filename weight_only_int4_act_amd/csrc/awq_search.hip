@@ -179,6 +179,13 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
         : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "memory");
 }
+// Lane J of each 16-lane row of v, for every lane of that row (DPP row_newbcast, folded by the
+// compiler into the consuming VALU instruction as a source modifier).
+template <int J>
+__device__ __forceinline__ float rowbcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xf, 0xf, true));
+}
+
 template <bool B>
 struct Flag {
     static constexpr bool value = B;
@@ -199,7 +206,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     constexpr int BM = NW * RBW * 16;    // token rows per workgroup
     constexpr int NWE = C * 128;         // 16-byte W entries of a group tile (float32)
     constexpr int NSE = NA * G / 4;      // 16-byte entries of NA scale rows of one group
-    constexpr int NSTG = NWE + 2 * NSE;  // staged 16-byte entries per group
+    constexpr int SPAD = 2;              // entries between scale and reciprocal rows (LDS banks)
+    constexpr int NSTG = NWE + 2 * NSE + SPAD;   // staged 16-byte entries per group
     constexpr int NSTGP = 2 * NW * 64;   // staging entries incl. padding (two per thread)
     static_assert(NW == 8 && NA < NW && NSTG <= NSTGP, "tile shape");
 
@@ -229,26 +237,36 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) acc[a][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // X fragments of this wavefront's rows for one whole group (C chunks x RBW row blocks), held in
-    // registers and loaded one group ahead: once the matrix-core work of chunk c of group jg has
-    // been issued, the same fragments receive chunk c of group jg + 1.  A load therefore has a whole
-    // group step to arrive.  Each load is one contiguous 1 KB block of the tiled X.
+    // X fragments of this wavefront's rows (RBW row blocks) for a few K chunks, held in register
+    // slots.  With 4 chunks per group there are 3 slots: chunks 0, 1, 2, 3 use slots 0, 1, 2, 0.
+    // The matrix-core half of group jg loads chunk 2 at its start, chunk 3 after chunk 0, chunk 1 of
+    // group jg + 1 after chunk 1 and chunk 0 of group jg + 1 after chunk 3, so every load has at
+    // least two chunks of matrix-core work (or the E half) to arrive while only two slots are live
+    // during the E half.  With 1 or 2 chunks per group the slots form a ring: chunk c's slot receives
+    // chunk c + XD once its products have been issued.  Each load is one contiguous 1 KB block of
+    // the tiled X.
     // The token tile's fragments form one contiguous range of (BM/16) * kchunks KB; a load takes
     // this lane's byte offset in a vector register and the row block and chunk as a scalar offset.
     const auto xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + (int64_t)tb * (BM / 16) * kchunks * 64), 0,
                                                          (BM / 16) * kchunks * 1024, 0x00020000);
     const uint32_t xvoff = ((uint32_t)(wave * RBW) * kchunks * 64 + lane) * 16;
-    u32x4 xr[C][RBW];
-    auto load_X = [&](int jg, int c) {
+    constexpr int XD = C >= 4 ? 3 : C >= 2 ? 2 : 1;
+    constexpr bool X3 = C == 4;
+    auto xslot = [](int c) { return X3 ? (c == 3 ? 0 : c) : c % XD; };
+    u32x4 xr[XD][RBW];
+    // chunk kc (counted over the whole K range, clamped to the last one) into ring slot `slot`
+    auto load_X = [&](int kc, int slot) {
+        kc = min(kc, kchunks - 1);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
-            xr[c][rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      xrsrc, xvoff, (rb * kchunks + jg * C + c) * 1024, 0));
+            xr[slot][rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         xrsrc, xvoff, (rb * kchunks + kc) * 1024, 0));
     };
 
     // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
-    // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  The
-    // padding entries re-read the last valid entry.
+    // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  SPAD
+    // entries between the scale and the reciprocal rows shift the latter by 8 LDS banks (they hold
+    // a copy of the first scale entry), and the entries past NSTG re-read the last valid entry.
     // The scale table, its reciprocals and the W tiles lie in one range of the workspace that
     // starts at s_tab (stage_bytes long, checked below 4 GB by the host); a transfer's source is a
     // byte offset in it that advances by a fixed step per group.
@@ -258,8 +276,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     for (int r = 0; r < 2; ++r) {
         const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
         const int es = e - NWE;
-        const int which = es >= NSE;                     // 0: scale row, 1: reciprocal row
-        const int idx = es - which * NSE;
+        const int which = es >= NSE + SPAD;              // 0: scale row (or padding), 1: reciprocal row
+        const int idx = which ? es - NSE - SPAD : (es < NSE ? es : 0);
         const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
         const char* src;
         if (e < NWE) {
@@ -290,23 +308,25 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // tie at one end of the range, where either neighbour has the same |error| = Delta/2.  The loss
     // is therefore unaffected up to the float32 rounding the search makes anyway; the packing
     // kernel applies the quantizer exactly, clamp included.
-    // The staged inputs are read two chunks ahead of their use (the W tile and scale rows in the
-    // range pass, the reciprocal rows in the quantization pass), so that LDS latency overlaps the
-    // arithmetic of the previous chunk.
-    const int srow = NWE + (slot * G) / 4;   // this slot's scale row in a staging buffer
-    u32x4 in[2][4];                          // W halves and scale halves of two chunks
+    // The staged inputs are read two chunks ahead of their use, so that LDS latency overlaps the
+    // arithmetic of the previous chunk.  The scale and reciprocal values of a chunk depend only on
+    // the row, and the 16 lanes of a quad (one 16-lane DPP row) need the same 8 rows: lane 16q + j
+    // reads the scale (j < 8) or the reciprocal (j >= 8) of row kmap(c, q) + (j & 7) with one 4-byte
+    // LDS read, and each multiply takes lane j's value of its row as a row_newbcast:j source.
+    const int srow = NWE + (slot * G) / 4;   // this slot's scale row (16-byte entries)
+    const int sidx = (r16 < 8 ? srow * 4 : (srow + NSE + SPAD) * 4) + (r16 & 7) + kmap<G>(0, q);
+    u32x4 in[2][2];                          // W halves of two chunks
+    float sv[C];                             // per chunk: this lane's scale or reciprocal
     auto fetch_in = [&](int ibuf, int c) {
         const u32x4* st = &Stg[ibuf][0];
         in[c & 1][0] = st[c * 128 + lane];
         in[c & 1][1] = st[c * 128 + 64 + lane];
-        in[c & 1][2] = st[srow + kmap<G>(c, q) / 4];
-        in[c & 1][3] = st[srow + kmap<G>(c, q) / 4 + 1];
+        sv[c] = ((const float*)st)[sidx + kmap<G>(c, 0)];
     };
-    // The first chunk's inputs are issued ahead of compute_E by the wavefronts whose matrix-core
-    // half comes first (inside its last chunk); compute_E issues the rest, two chunks ahead.
+    // The first chunk's inputs are issued ahead of compute_E, inside a matrix-core half;
+    // compute_E issues the rest, two chunks ahead.
     auto prefetch_E = [&](int ibuf) { fetch_in(ibuf, 0); };
     auto compute_E = [&](int ibuf, int ebuf, bool prefetched) {
-        const u32x4* st = &Stg[ibuf][0];
         float pk[C * 8];
         // ZP: mx = max(p, 0) and nmn = -min(p, 0) (the group range always includes 0); else
         // mx = max |p|
@@ -318,15 +338,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         for (int c = 0; c < C; ++c) {
             const floatx4 w0 = __builtin_bit_cast(floatx4, in[c & 1][0]);
             const floatx4 w1 = __builtin_bit_cast(floatx4, in[c & 1][1]);
-            const floatx4 s0 = __builtin_bit_cast(floatx4, in[c & 1][2]);
-            const floatx4 s1 = __builtin_bit_cast(floatx4, in[c & 1][3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pk[c * 8 + j] = s0[j] * w0[j];
-                pk[c * 8 + 4 + j] = s1[j] * w1[j];
-            }
+            float* v = &pk[c * 8];
+            v[0] = rowbcast<0>(sv[c]) * w0[0];
+            v[1] = rowbcast<1>(sv[c]) * w0[1];
+            v[2] = rowbcast<2>(sv[c]) * w0[2];
+            v[3] = rowbcast<3>(sv[c]) * w0[3];
+            v[4] = rowbcast<4>(sv[c]) * w1[0];
+            v[5] = rowbcast<5>(sv[c]) * w1[1];
+            v[6] = rowbcast<6>(sv[c]) * w1[2];
+            v[7] = rowbcast<7>(sv[c]) * w1[3];
             if (c + 2 < C) fetch_in(ibuf, c + 2);
-            const float* v = &pk[c * 8];
             if (ZP) {
                 cmx[c] = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), fmaxf(v[6], v[7]));
                 cmn[c] = max3f(nmax3f(v[0], v[1], v[2]), nmax3f(v[3], v[4], v[5]), nmaxf(v[6], v[7]));
@@ -340,13 +361,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             mx = fmaxf(mx, cmx[c]);
             if (ZP) nmn = fmaxf(nmn, cmn[c]);
         }
-        u32x4 iv[2][2];             // reciprocal-row halves of two chunks
-        auto fetch_inv = [&](int c) {
-            iv[c & 1][0] = st[srow + NSE + kmap<G>(c, q) / 4];
-            iv[c & 1][1] = st[srow + NSE + kmap<G>(c, q) / 4 + 1];
-        };
-        fetch_inv(0);
-        if constexpr (C > 1) fetch_inv(1);
         float d;
         if (ZP) {
             quad_max2(mx, nmn);
@@ -361,16 +375,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const float rd = __builtin_amdgcn_rcpf(d);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const floatx4 i0 = __builtin_bit_cast(floatx4, iv[c & 1][0]);
-            const floatx4 i1 = __builtin_bit_cast(floatx4, iv[c & 1][1]);
-            float e[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float pv = pk[c * 8 + j];
-                const float lv = rintf(pv * rd);
-                e[j] = fmaf(lv, d, -pv) * (j < 4 ? i0[j] : i1[j - 4]);   // (level*Delta - s*w) / s
-            }
-            if (c + 2 < C) fetch_inv(c + 2);
+            const float* v = &pk[c * 8];
+            float e[8];   // (level*Delta - s*w) / s
+            e[0] = fmaf(rintf(v[0] * rd), d, -v[0]) * rowbcast<8>(sv[c]);
+            e[1] = fmaf(rintf(v[1] * rd), d, -v[1]) * rowbcast<9>(sv[c]);
+            e[2] = fmaf(rintf(v[2] * rd), d, -v[2]) * rowbcast<10>(sv[c]);
+            e[3] = fmaf(rintf(v[3] * rd), d, -v[3]) * rowbcast<11>(sv[c]);
+            e[4] = fmaf(rintf(v[4] * rd), d, -v[4]) * rowbcast<12>(sv[c]);
+            e[5] = fmaf(rintf(v[5] * rd), d, -v[5]) * rowbcast<13>(sv[c]);
+            e[6] = fmaf(rintf(v[6] * rd), d, -v[6]) * rowbcast<14>(sv[c]);
+            e[7] = fmaf(rintf(v[7] * rd), d, -v[7]) * rowbcast<15>(sv[c]);
             if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
                 Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                                                 pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
@@ -379,26 +393,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 
     // Matrix-core work of one group: for each chunk and alpha, the RBW products with this wavefront's
     // X fragments; the E fragment of an alpha for the next chunk is read from LDS as soon as the
-    // current one has been consumed, and the X fragments of chunk c < C-1 are reloaded with the next
-    // group's as soon as the chunk's products have been issued.  The last chunk of a group (when a
-    // group has several) is loaded at the start of the group's own matrix-core work instead, three
-    // chunks ahead of its use, so that its registers are free during the E computation.
-    constexpr int CL = C > 1 ? C - 1 : C;   // chunks loaded one group ahead
+    // current one has been consumed, and the chunk's X registers are reloaded XD chunks ahead as soon
+    // as its products have been issued.
     // The staging transfers of a step are issued inside the matrix-core half, after chunk SC, where
     // their issue cost hides behind the matrix work; XS = X loads of the half issued before them.
     constexpr int SC = C >= 4 ? 1 : 0;
-    constexpr int XS = (C > 1 ? RBW : 0) + (SC + 1) * RBW;
+    constexpr int XS = (SC + 1 + (X3 ? 1 : 0)) * RBW;
     // PRE: after the products of alpha NA-2 in the last chunk (when the other alphas' E fragments
     // are dead), issue the LDS reads of the first inputs of an E computation (staged in Stg[pbuf]).
     auto mfma_group = [&](auto pre_tag, int jg, int buf, int sjg, int sbuf, int pbuf) {
         constexpr bool PRE = decltype(pre_tag)::value;
         constexpr int PA = NA > 2 ? NA - 2 : 0;
-        const int jn = min(jg + 1, n_groups - 1);
-        if constexpr (C > 1) load_X(jg, C - 1);
+        if constexpr (X3) load_X(jg * C + 2, 2);
         u32x4 B[NA];
 #pragma unroll
         for (int a = 0; a < NA; ++a) B[a] = Es[buf][a][0][lane];
-        if constexpr (C > 1) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
+        if constexpr (X3) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);      // VMEM read
         __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);                         // DS read
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -406,12 +416,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             for (int a = 0; a < NA; ++a) {
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb)
-                    acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, xr[c][rb]), __builtin_bit_cast(bf16x8, B[a]),
-                                              acc[a][rb]);
+                    acc[a][rb] = mfma16x16x32(__builtin_bit_cast(bf16x8, xr[xslot(c)][rb]),
+                                              __builtin_bit_cast(bf16x8, B[a]), acc[a][rb]);
                 if (c + 1 < C) B[a] = Es[buf][a][c + 1 < C ? c + 1 : 0][lane];
                 if (PRE && c == C - 1 && a == PA) prefetch_E(pbuf);
             }
-            if (c < CL) load_X(jn, c);
+            if constexpr (X3) {
+                if (c == 0) load_X(jg * C + 3, 0);
+                if (c == 1) load_X(jg * C + C + 1, 1);
+                if (c == 3) load_X(jg * C + C, 0);
+            } else {
+                load_X(jg * C + c + XD, c % XD);
+            }
             // issue order inside the chunk: per alpha, its RBW products then the next chunk's E
             // fragment read; the X reloads last.  Keeps one E fragment set and one X set live.
 #pragma unroll
@@ -421,15 +437,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                 if (PRE && c == C - 1 && a == PA)
                     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
             }
-            if (c < CL) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
+            if (!X3 || c != 2) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
             __builtin_amdgcn_sched_barrier(0);
             if (c == SC) stage(sjg, sbuf);
         }
     };
 
-    // ---- prologue: X of group 0 in registers, inputs of groups 0-3 staged, E(0) computed.
+    // ---- prologue: the first X chunks in registers, inputs of groups 0-3 staged, E(0) computed.
 #pragma unroll
-    for (int c = 0; c < CL; ++c) load_X(0, c);
+    for (int c = 0; c < (X3 ? 2 : XD); ++c) load_X(c, c);
 #pragma unroll
     for (int g = 0; g < 4; ++g) stage(min(g, n_groups - 1), g);
     wait_vmcnt<0>();
@@ -468,7 +484,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn);
             compute_E(sbn, buf ^ 1, true);
         } else {
-            compute_E(sbn, buf ^ 1, true);
+            // the spare wavefront (no alpha slot of its own) skips the E half
+            if (wave < NA) compute_E(sbn, buf ^ 1, true);
             mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn2);
         }
         wait_vmcnt<2 * C * RBW - XS + 2>();
@@ -543,27 +560,30 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ losse
 
 namespace {
 
-// Instantiations: (group size, zero point) x one tile shape.
-// 8 wavefronts (2 per SIMD), 4 row blocks of 16 each -> 512 token rows per workgroup, 7 alphas
-// per workgroup (21 = 3 slices of 7).  Accumulators: 7 x 4 x 4 = 112 VGPRs per lane.
-constexpr int kNA = 7, kRBW = 4, kNW = 8;
-constexpr int kBM = kNW * kRBW * 16;
+// Instantiations: (group size, zero point) x two tile shapes.  8 wavefronts (2 per SIMD), 7 alphas
+// per workgroup (21 = 3 slices of 7), and RBW row blocks of 16 per wavefront: RBW = 5 (640 token
+// rows, 140 accumulator VGPRs per lane) halves the E work per product against RBW = 4 (512 rows) by
+// a fifth; the plan takes it unless padding the tokens to 640-row tiles costs more than that.
+constexpr int kNA = 7, kNW = 8;
 
 typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, uint32_t,
                           int, int, int, int, double*);
 
-search_fn pick(int g, int zp) {
+template <int RBW>
+search_fn pick_rbw(int g, int zp) {
     if (zp) {
-        if (g == 32) return k_search<32, kNA, kRBW, kNW, true>;
-        if (g == 64) return k_search<64, kNA, kRBW, kNW, true>;
-        if (g == 128) return k_search<128, kNA, kRBW, kNW, true>;
+        if (g == 32) return k_search<32, kNA, RBW, kNW, true>;
+        if (g == 64) return k_search<64, kNA, RBW, kNW, true>;
+        if (g == 128) return k_search<128, kNA, RBW, kNW, true>;
     } else {
-        if (g == 32) return k_search<32, kNA, kRBW, kNW, false>;
-        if (g == 64) return k_search<64, kNA, kRBW, kNW, false>;
-        if (g == 128) return k_search<128, kNA, kRBW, kNW, false>;
+        if (g == 32) return k_search<32, kNA, RBW, kNW, false>;
+        if (g == 64) return k_search<64, kNA, RBW, kNW, false>;
+        if (g == 128) return k_search<128, kNA, RBW, kNW, false>;
     }
     return nullptr;
 }
+
+search_fn pick(int g, int zp, int rbw) { return rbw == 5 ? pick_rbw<5>(g, zp) : pick_rbw<4>(g, zp); }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -574,12 +594,15 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     p.group_size = group_size;
     p.n_grid = n_grid;
     p.zero_point = zero_point;
-    p.variant = 0;
+    // rows per workgroup: 640 (RBW = 5) unless its padding of T exceeds 512-row tiles' by more than
+    // the ~4.5% it gains per row (measured on the 4096x4096 layer)
+    const int64_t pad5 = (T + 639) / 640 * 640, pad4 = (T + 511) / 512 * 512;
+    p.variant = pad5 * 1000 <= pad4 * 1045 ? 5 : 4;   // row blocks per wavefront
     p.na = kNA;
-    p.bm = kBM;
+    p.bm = p.variant * kNW * 16;
     p.n_asplit = (n_grid + kNA - 1) / kNA;
     p.nb = (N + 15) / 16;
-    p.tb = (T + kBM - 1) / kBM;
+    p.tb = (T + p.bm - 1) / p.bm;
     p.tiles = p.tb * p.nb * p.n_asplit;
     p.tiles_per_xcd = (p.tiles + kNumXcd - 1) / kNumXcd;
     p.grid = p.tiles_per_xcd * kNumXcd;
@@ -587,7 +610,7 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     p.off_s = off;    off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_inv = off;  off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(float));
-    p.off_xt = off;   off = align256(off + (size_t)p.tb * kBM * K * sizeof(uint16_t));
+    p.off_xt = off;   off = align256(off + (size_t)p.tb * p.bm * K * sizeof(uint16_t));
     p.off_part = off; off = align256(off + (size_t)p.tb * p.nb * n_grid * sizeof(double));
     p.ws_bytes = off;
     return p;
@@ -611,13 +634,13 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
     else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t xtotal = p.tb * (kBM / 16) * (K / 32) * 64;
+    const int64_t xtotal = p.tb * (p.bm / 16) * (K / 32) * 64;
     const unsigned xgrid = (unsigned)((xtotal + 255) / 256);
     if (p.group_size == 32) k_tile_x<32><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
     else if (p.group_size == 64) k_tile_x<64><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
     else k_tile_x<128><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    search_fn fn = pick(p.group_size, p.zero_point);
+    search_fn fn = pick(p.group_size, p.zero_point, p.variant);
     if (!fn) return hipErrorInvalidValue;
     const uint32_t stage_bytes = (uint32_t)(p.off_xt - p.off_s);   // scale table, reciprocals, W tiles
     fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, stage_bytes,
