@@ -28,6 +28,8 @@ Sources (page title -- section):
   weights per byte.
 * [P5] "量化推理算法 GPTQ / AWQ" (slowleelab) -- 4.3 AWQ search loop (keep the
   best loss with a strict "<", so the first minimum wins).
+* [P4] 架构 and 关键设计 5: the config carries an optional clip_ratio, a min-max
+  clipping of the group range applied before the search (default: none).
 
 Readings where the pages are silent or disagree (each is listed with its reason
 in the design notes of the repository):
@@ -42,7 +44,11 @@ in the design notes of the repository):
   stored code = level + 8, zero = 8 (so one dequant formula (code - zero)*Delta serves both);
 * rounding is round-half-to-even;
 * loss is the plain sum of squares ||X (What - W)||^2, argmin takes the smallest alpha
-  among equal losses.
+  among equal losses;
+* clipping with ratio c in (0, 1] multiplies both ends of the group range (0 included)
+  by c before Delta and zero are formed; codes beyond the clipped range clamp to its end
+  levels; c = 1 is the unclipped quantizer.  A clip search scores c_j = 1 - (1 - c_min)
+  j/(n-1), j = 0..n-1, at fixed scales s with the same loss and takes the first minimum.
 
 No function here is "parity unpinned": each is pinned by tests under
 ``tests/test_oracle_*.py`` against worked values, closed forms, invariants and
@@ -92,12 +98,13 @@ def scale_table(mean_abs: np.ndarray, n_grid: int = 21) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- quantizer
-def quantize_groups(P: np.ndarray, group_size: int, zero_point: bool):
+def quantize_groups(P: np.ndarray, group_size: int, zero_point: bool, clip: float = 1.0):
     """Group-wise INT4 quantization of P (float64 [K, N]) along K, per output column.
 
     [P1] 量化数学基础 (per-group step, round, clamp), [P3] section 4 (symmetric
     absmax: Delta = max|w_s| / (2**(b-1) - 1) = max|w_s|/7), [P2] section 2
-    (``zero_point`` selects the min-max form with a zero point).
+    (``zero_point`` selects the min-max form with a zero point), [P4] 关键设计 5
+    (optional min-max clipping: ``clip`` scales both ends of the range, float64).
 
     Returns (codes int64 [K, N] in 0..15, delta float32 [K/g, N], zero int64 [K/g, N]).
     The dequantized value of an element is (code - zero) * delta.
@@ -105,17 +112,18 @@ def quantize_groups(P: np.ndarray, group_size: int, zero_point: bool):
     P = np.asarray(P, dtype=np.float64)
     K, N = P.shape
     g = int(group_size)
+    c = float(np.float32(clip))
     G = P.reshape(K // g, g, N)
     if zero_point:
-        mx = np.maximum(G.max(axis=1), 0.0)
-        mn = np.minimum(G.min(axis=1), 0.0)
+        mx = np.maximum(G.max(axis=1), 0.0) * c
+        mn = np.minimum(G.min(axis=1), 0.0) * c
         delta = ((mx - mn) / 15.0).astype(np.float32)
         delta[delta == 0] = 1.0
         d = delta.astype(np.float64)
         zero = np.clip(np.rint(-mn / d), 0, 15)
         codes = np.clip(np.rint(G / d[:, None, :]) + zero[:, None, :], 0, 15)
     else:
-        amax = np.abs(G).max(axis=1)
+        amax = np.abs(G).max(axis=1) * c
         delta = (amax / 7.0).astype(np.float32)
         delta[delta == 0] = 1.0
         d = delta.astype(np.float64)
@@ -124,7 +132,8 @@ def quantize_groups(P: np.ndarray, group_size: int, zero_point: bool):
     return codes.reshape(K, N).astype(np.int64), delta, zero.astype(np.int64)
 
 
-def pre_round_values(P: np.ndarray, delta: np.ndarray, group_size: int, zero_point: bool):
+def pre_round_values(P: np.ndarray, delta: np.ndarray, group_size: int, zero_point: bool,
+                     clip: float = 1.0):
     """The values that the quantizer rounds: p/Delta per element and, for the
     asymmetric form, -min/Delta per group.  Used only to count near-ties."""
     P = np.asarray(P, dtype=np.float64)
@@ -134,7 +143,7 @@ def pre_round_values(P: np.ndarray, delta: np.ndarray, group_size: int, zero_poi
     t = P / d
     if zero_point:
         G = P.reshape(K // g, g, N)
-        mn = np.minimum(G.min(axis=1), 0.0)
+        mn = np.minimum(G.min(axis=1), 0.0) * float(np.float32(clip))
         tz = -mn / delta.astype(np.float64)
     else:
         tz = np.zeros(delta.shape)
@@ -156,7 +165,7 @@ def dequantize(codes: np.ndarray, delta: np.ndarray, zero: np.ndarray, group_siz
 
 
 def fake_quant(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
-               quantizer=None) -> np.ndarray:
+               quantizer=None, clip: float = 1.0) -> np.ndarray:
     """What = S^-1 Q(S W): [P1] step 4a-4b and [P5] 4.3 (What = quant(W diag(s)) diag(s)^-1).
 
     ``W`` float64 [K, N] (input channel k is row k), ``s`` float32/64 [K].
@@ -168,7 +177,7 @@ def fake_quant(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
     s64 = np.asarray(s, dtype=np.float64)
     P = s64[:, None] * W
     if quantizer is None:
-        codes, delta, zero = quantize_groups(P, group_size, zero_point)
+        codes, delta, zero = quantize_groups(P, group_size, zero_point, clip)
         Ph = dequantize(codes, delta, zero, group_size)
     else:
         Ph = quantizer(P)
@@ -177,18 +186,32 @@ def fake_quant(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
 
 # ----------------------------------------------------------------------------- a3/a4
 def loss(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
-         quantizer=None) -> float:
+         quantizer=None, clip: float = 1.0) -> float:
     """L = ||X (S^-1 Q(S W) - W)||^2: [P1] step 4c, with the error analysis of
     AWQ 的缩放如何改变量化误差 (Delta Y = X S^-1 eps_SW)."""
-    E = fake_quant(W, s, group_size, zero_point, quantizer) - np.asarray(W, dtype=np.float64)
+    E = fake_quant(W, s, group_size, zero_point, quantizer, clip) - np.asarray(W, dtype=np.float64)
     Y = np.asarray(X, dtype=np.float64) @ E
     return float(np.sum(Y * Y))
 
 
 def losses(X: np.ndarray, W: np.ndarray, S: np.ndarray, group_size: int, zero_point: bool,
-           quantizer=None) -> np.ndarray:
+           quantizer=None, clip: float = 1.0) -> np.ndarray:
     """L(alpha_i) for every row s_i of the scale table S [n_grid, K]."""
-    return np.array([loss(X, W, S[i], group_size, zero_point, quantizer) for i in range(S.shape[0])])
+    return np.array([loss(X, W, S[i], group_size, zero_point, quantizer, clip) for i in range(S.shape[0])])
+
+
+def clip_grid(clip_min: float, n: int) -> np.ndarray:
+    """Clip ratios c_j = fl32(1 - (1 - c_min) * j / (n - 1)), j = 0..n-1, in float64 before
+    the rounding; c_0 = 1 (no clipping) comes first, so ties keep the unclipped quantizer."""
+    cm = float(np.float32(clip_min))
+    return np.array([np.float32(1.0 - (1.0 - cm) * j / (n - 1)) for j in range(n)], dtype=np.float32)
+
+
+def clip_losses(X: np.ndarray, W: np.ndarray, s: np.ndarray, ratios: np.ndarray, group_size: int,
+                zero_point: bool) -> np.ndarray:
+    """L(c_j) = ||X (S^-1 Q_c_j(S W) - W)||^2 at fixed scales s, for every clip ratio: the
+    loss of [P1] step 4c with the clipped quantizer of [P4] 关键设计 5."""
+    return np.array([loss(X, W, s, group_size, zero_point, clip=float(c)) for c in ratios])
 
 
 def select(L: np.ndarray) -> int:
@@ -238,11 +261,11 @@ def unpack_nibbles(words: np.ndarray) -> np.ndarray:
     return out.reshape(Kw * 8, N)
 
 
-def pack(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool):
+def pack(W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool, clip: float = 1.0):
     """Offline quantization W_q = Quantize(diag(s*) W) ([P1] 推理时的等效实现),
     stored as (codes uint32 [K/8, N], scales float32 [K/g, N], zeros uint8 [K/g, N])."""
     P = np.asarray(s, dtype=np.float64)[:, None] * np.asarray(W, dtype=np.float64)
-    codes, delta, zero = quantize_groups(P, group_size, zero_point)
+    codes, delta, zero = quantize_groups(P, group_size, zero_point, clip)
     return pack_nibbles(codes), delta.astype(np.float32), zero.astype(np.uint8)
 
 
