@@ -44,7 +44,8 @@ extern "C" {
 
 #define AWQ_OK 0
 #define AWQ_ERR_INVALID_ARG (-1) /* null/misaligned pointer, non-positive size, K % group_size != 0, ... */
-#define AWQ_ERR_UNSUPPORTED (-2) /* w_bit != 4, group_size not in {32, 64, 128}, n_grid outside [2, 64] */
+#define AWQ_ERR_UNSUPPORTED (-2) /* w_bit != 4, group_size not in {32, 64, 128}, n_grid outside [2, 64],
+                                    clip_ratio outside [0, 1] */
 #define AWQ_ERR_WORKSPACE (-3)   /* workspace smaller than the matching *_workspace_size() */
 #define AWQ_ERR_HIP (-4)         /* a HIP call failed; awq_last_hip_error() holds its code */
 
@@ -60,13 +61,22 @@ extern "C" {
  *               In both modes Delta := 1 when the group is all zero, and the dequantized
  *               value is (code - zero) * Delta.
  *   n_grid      number of alpha points, alpha_i = i/(n_grid-1) ([P1] 缩放因子优化的完整流程
- *               step 3 uses 21: {0, 0.05, ..., 1}).  Supported: 2..64.
+ *               step 3 uses 21: {0, 0.05, ..., 1}).  Supported: 2..64.  awq_clip_search
+ *               reads it as the number of clip ratios.
+ *   clip_ratio  min-max clipping of the group range before quantization ([P4] 架构,
+ *               AWQConfig.clip_ratio; 关键设计 5, applied before the search): both ends of the
+ *               range (0 included; max|p| in symmetric mode) are multiplied by c before Delta
+ *               and the zero are formed, and codes beyond the clipped range clamp to its end
+ *               levels.  0 or 1 = no clipping (so a zero-initialised struct needs no value);
+ *               values in (0, 1) clip.  awq_search and awq_pack use it; awq_clip_search
+ *               ignores it.
  */
 typedef struct awq_qconfig {
     int32_t w_bit;
     int32_t group_size;
     int32_t zero_point;
     int32_t n_grid;
+    float clip_ratio;
 } awq_qconfig;
 
 /* ---------------------------------------------------------------- a1: statistic
@@ -126,6 +136,22 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
  */
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg,
              uint32_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/* ---------------------------------------------------------------- clip search
+ * The search of awq_search with the alpha grid replaced by a grid of clip ratios at fixed
+ * scales s (normally s_best): for c_j = float32(1 - (1 - clip_min) * j / (n - 1)),
+ * j = 0..n-1 with n = cfg->n_grid (evaluated in float64; c_0 = 1 is the unclipped quantizer),
+ *   L_j = || X (S^-1 Q_cj(S W) - W) ||^2,
+ * with Q_c the quantizer of awq_qconfig clipped by c ([P4] 关键设计 5 and AWQConfig.clip_ratio;
+ * the loss of [P1] 缩放因子优化的完整流程 step 4c); the first minimum wins ([P5] 4.3).
+ *   X  bf16 [T, K];  W  bf16 [K, N];  s  float32 [K] (device);  clip_min in (0, 1].
+ *   losses  float64 [n] out;  best  int32 [1] out;  clip_best  float32 [1] out (c_best).
+ *   workspace >= awq_search_workspace_size(T, K, N, cfg) bytes (the same layout).
+ * Pass clip_best as cfg->clip_ratio to awq_pack to store the clipped quantization.
+ */
+int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N,
+                    const float* s, const awq_qconfig* cfg, float clip_min, void* workspace,
+                    size_t ws_bytes, double* losses, int32_t* best, float* clip_best, void* stream);
 
 /* ---------------------------------------------------------------- a6: W4A16 product
  * Y[m, n] = sum_k (x_mk / s_k) * (code_kn - zero_gn) * Delta_gn,  g = k / group_size

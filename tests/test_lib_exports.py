@@ -75,6 +75,18 @@ def test_host_validation_rejects_before_launch(awq):
     need = awq.awq_search_workspace_size(8, 128, 16, cfg)
     assert lib.awq_search(p, 8, p, 128, 16, p, ctypes.byref(cfg), p, need - 1, p, p, p,
                           nul) == awq.AWQ_ERR_WORKSPACE
+    # clipping: ratio outside [0, 1] (NaN included) in the configuration, clip_min outside (0, 1]
+    for c in (1.5, -0.1, float("nan")):
+        bad = awq.qconfig(128, True, 21, clip_ratio=c)
+        assert lib.awq_search(p, 8, p, 128, 16, p, ctypes.byref(bad), p, ws, p, p, p, nul) == awq.AWQ_ERR_UNSUPPORTED
+        assert lib.awq_pack(p, 128, 16, p, ctypes.byref(bad), p, p, p, nul) == awq.AWQ_ERR_UNSUPPORTED
+    for cm in (0.0, -0.5, 1.01, float("nan")):
+        assert lib.awq_clip_search(p, 8, p, 128, 16, p, ctypes.byref(cfg), ctypes.c_float(cm), p, ws, p, p, p,
+                                   nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_clip_search(p, 8, p, 128, 16, nul, ctypes.byref(cfg), ctypes.c_float(0.5), p, ws, p, p, p,
+                               nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_clip_search(p, 8, p, 128, 16, p, ctypes.byref(cfg), ctypes.c_float(0.5), p, need - 1, p, p, p,
+                               nul) == awq.AWQ_ERR_WORKSPACE
     # stats
     assert lib.awq_act_stats(p, 8, 16, nul, 0, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_act_stats(p, 8, 16, p, 0, 7, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG   # total < T

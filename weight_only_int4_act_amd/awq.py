@@ -33,11 +33,12 @@ class AwqError(RuntimeError):
 
 class awq_qconfig(ctypes.Structure):
     _fields_ = [("w_bit", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("zero_point", ctypes.c_int32), ("n_grid", ctypes.c_int32)]
+                ("zero_point", ctypes.c_int32), ("n_grid", ctypes.c_int32), ("clip_ratio", ctypes.c_float)]
 
 
-def qconfig(group_size: int = 128, zero_point: bool = True, n_grid: int = 21, w_bit: int = 4) -> awq_qconfig:
-    return awq_qconfig(int(w_bit), int(group_size), 1 if zero_point else 0, int(n_grid))
+def qconfig(group_size: int = 128, zero_point: bool = True, n_grid: int = 21, w_bit: int = 4,
+            clip_ratio: float = 1.0) -> awq_qconfig:
+    return awq_qconfig(int(w_bit), int(group_size), 1 if zero_point else 0, int(n_grid), float(clip_ratio))
 
 
 _P = ctypes.c_void_p
@@ -53,6 +54,7 @@ _SIGNATURES = {
     "awq_search_workspace_size": (_SZ, [_I64, _I64, _I64, _CFG]),
     "awq_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
     "awq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _CFG, _P, _P, _P, _P]),
+    "awq_clip_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, ctypes.c_float, _P, _SZ, _P, _P, _P, _P]),
     "awq_w4a16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "awq_w4a16_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -149,6 +151,18 @@ def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, codes: torch.Te
     K, N = W.shape
     _check("awq_pack", _lib.awq_pack(_ptr(W), K, N, _ptr(s), ctypes.byref(cfg), _ptr(codes), _ptr(scales),
                                      _ptr(zeros), _stream(stream)))
+
+
+def awq_clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, clip_min: float,
+                    ws: torch.Tensor, losses: torch.Tensor, best: torch.Tensor, clip_best: torch.Tensor,
+                    stream=None) -> None:
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [T, {K}] but W is [{K2}, N]")
+    _check("awq_clip_search", _lib.awq_clip_search(_ptr(X), T, _ptr(W), K, N, _ptr(s), ctypes.byref(cfg),
+                                                   float(clip_min), _ptr(ws), _nbytes(ws), _ptr(losses),
+                                                   _ptr(best), _ptr(clip_best), _stream(stream)))
 
 
 def awq_w4a16_gemm_workspace_size(M: int, K: int, N: int, group_size: int) -> int:

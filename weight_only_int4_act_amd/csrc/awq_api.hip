@@ -23,6 +23,7 @@ int check_cfg(const awq_qconfig* cfg, int64_t K) {
     if (!group_ok(cfg->group_size)) return AWQ_ERR_UNSUPPORTED;
     if (cfg->n_grid < 2 || cfg->n_grid > 64) return AWQ_ERR_UNSUPPORTED;
     if (cfg->zero_point != 0 && cfg->zero_point != 1) return AWQ_ERR_INVALID_ARG;
+    if (!(cfg->clip_ratio >= 0.f && cfg->clip_ratio <= 1.f)) return AWQ_ERR_UNSUPPORTED;   // NaN fails too
     if (K % cfg->group_size != 0) return AWQ_ERR_INVALID_ARG;
     return AWQ_OK;
 }
@@ -58,30 +59,58 @@ int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_t
 
 size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg) {
     if (T <= 0 || K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
-    return awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid).ws_bytes;
+    return awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid, false).ws_bytes;
 }
+
+namespace {
+
+// Checks shared by both searches; 0 when the call may go ahead.
+int check_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* vec,
+                 const awq_qconfig* cfg, void* workspace, size_t ws_bytes, const double* losses, const int32_t* best,
+                 const float* out, bool clip, awq::SearchPlan* p) {
+    if (!X_bf16 || !W_bf16 || !vec || !losses || !best || !out) return AWQ_ERR_INVALID_ARG;
+    if (T <= 0 || K <= 0 || N <= 0 || T * K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
+    int st = check_cfg(cfg, K);
+    if (st != AWQ_OK) return st;
+    if (!aligned(X_bf16, 16) || !aligned(W_bf16, 2) || !aligned(vec, 4) || !aligned(losses, 8) ||
+        !aligned(best, 4) || !aligned(out, 4))
+        return AWQ_ERR_INVALID_ARG;
+    *p = awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid, clip);
+    // tile counts and the 16-byte index into the tiled copy of X are 32-bit in the kernel; the
+    // kernel addresses the staged inputs (scale table, reciprocals, W tiles) and one token tile of
+    // tiled X through buffer resources with 32-bit byte offsets
+    if (p->tiles > kIntMax || p->tb * p->bm * K / 8 > kIntMax ||
+        (int64_t)(p->off_xt - p->off_s) > (int64_t)0xffffffff || (int64_t)p->bm * K * 2 > kIntMax)
+        return AWQ_ERR_INVALID_ARG;
+    if (ws_bytes < p->ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
+    return AWQ_OK;
+}
+
+}  // namespace
 
 int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* mean_abs,
                const awq_qconfig* cfg, void* workspace, size_t ws_bytes, double* losses, int32_t* best,
                float* s_best, void* stream) {
-    if (!X_bf16 || !W_bf16 || !mean_abs || !losses || !best || !s_best) return AWQ_ERR_INVALID_ARG;
-    if (T <= 0 || K <= 0 || N <= 0 || T * K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
-    int st = check_cfg(cfg, K);
+    awq::SearchPlan p;
+    const bool clip = cfg && cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f;
+    const int st =
+        check_search(X_bf16, T, W_bf16, K, N, mean_abs, cfg, workspace, ws_bytes, losses, best, s_best, clip, &p);
     if (st != AWQ_OK) return st;
-    if (!aligned(X_bf16, 16) || !aligned(W_bf16, 2) || !aligned(mean_abs, 4) || !aligned(losses, 8) ||
-        !aligned(best, 4) || !aligned(s_best, 4))
-        return AWQ_ERR_INVALID_ARG;
-    const awq::SearchPlan p = awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid);
-    // tile counts and the 16-byte index into the tiled copy of X are 32-bit in the kernel
-    // the kernel addresses the staged inputs (scale table, reciprocals, W tiles) and one token tile
-    // of tiled X through buffer resources with 32-bit byte offsets
-    if (p.tiles > kIntMax || p.tb * p.bm * K / 8 > kIntMax || (int64_t)(p.off_xt - p.off_s) > (int64_t)0xffffffff ||
-        (int64_t)p.bm * K * 2 > kIntMax)
-        return AWQ_ERR_INVALID_ARG;
-    if (ws_bytes < p.ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
-    return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs, p,
-                                         workspace, losses, best, s_best, (hipStream_t)stream));
+    return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs,
+                                         cfg->clip_ratio, p, workspace, losses, best, s_best, (hipStream_t)stream));
+}
+
+int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* s,
+                    const awq_qconfig* cfg, float clip_min, void* workspace, size_t ws_bytes, double* losses,
+                    int32_t* best, float* clip_best, void* stream) {
+    if (!(clip_min > 0.f && clip_min <= 1.f)) return AWQ_ERR_INVALID_ARG;
+    awq::SearchPlan p;
+    const int st =
+        check_search(X_bf16, T, W_bf16, K, N, s, cfg, workspace, ws_bytes, losses, best, clip_best, true, &p);
+    if (st != AWQ_OK) return st;
+    return hip_status(awq::launch_clip_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, s,
+                                              clip_min, p, workspace, losses, best, clip_best, (hipStream_t)stream));
 }
 
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg, uint32_t* codes,
@@ -92,8 +121,8 @@ int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq
     if (K / cfg->group_size > 65535) return AWQ_ERR_INVALID_ARG;
     if (!aligned(W_bf16, 2) || !aligned(s, 4) || !aligned(codes, 4) || !aligned(scales, 4))
         return AWQ_ERR_INVALID_ARG;
-    return hip_status(awq::launch_pack((const uint16_t*)W_bf16, K, N, s, cfg->group_size, cfg->zero_point, codes,
-                                       scales, zeros, (hipStream_t)stream));
+    return hip_status(awq::launch_pack((const uint16_t*)W_bf16, K, N, s, cfg->group_size, cfg->zero_point,
+                                       cfg->clip_ratio, codes, scales, zeros, (hipStream_t)stream));
 }
 
 size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size) {
@@ -122,7 +151,7 @@ const char* awq_status_string(int status) {
     switch (status) {
         case AWQ_OK: return "ok";
         case AWQ_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or shape)";
-        case AWQ_ERR_UNSUPPORTED: return "unsupported configuration (w_bit, group_size or n_grid)";
+        case AWQ_ERR_UNSUPPORTED: return "unsupported configuration (w_bit, group_size, n_grid or clip_ratio)";
         case AWQ_ERR_WORKSPACE: return "workspace too small";
         case AWQ_ERR_HIP: return "HIP runtime error (see awq_last_hip_error)";
         default: return "unknown status";

@@ -6,6 +6,8 @@
 
 namespace awq {
 
+constexpr int kMaxGrid = 64;   // largest alpha / clip-ratio grid
+
 // ---- a1: statistic
 struct StatsPlan {
     int64_t col_blocks;      // workgroups along K (512 channels each)
@@ -32,17 +34,26 @@ struct SearchPlan {
     int64_t nb;              // 16-column blocks (N rounded up)
     int64_t tb;              // token blocks
     int64_t tiles, tiles_per_xcd, grid;
-    // workspace layout (byte offsets)
-    size_t off_s, off_inv, off_wt, off_xt, off_part, ws_bytes;
+    // workspace layout (byte offsets): scale table, reciprocals, W tiles, X tiles, loss partials,
+    // clip ratio per grid point
+    size_t off_s, off_inv, off_wt, off_xt, off_part, off_clip, ws_bytes;
 };
-SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid);
+// clip: the quantizer is clipped (awq_clip_search, or awq_search with a clip ratio); the workspace
+// layout does not depend on it
+SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid, bool clip);
+// alpha grid from mean_abs, every point's quantizer clipped by clip_ratio (0 or 1: none)
 hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
-                         const float* mean_abs, const SearchPlan& p, void* ws, double* losses,
+                         const float* mean_abs, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
                          int32_t* best, float* s_best, hipStream_t st);
+// clip-ratio grid 1 .. clip_min at the fixed scales s
+hipError_t launch_clip_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                              const float* s, float clip_min, const SearchPlan& p, void* ws, double* losses,
+                              int32_t* best, float* clip_best, hipStream_t st);
 
-// ---- a5: pack
+// ---- a5: pack (clip_ratio 0 or 1: no clipping)
 hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, int group_size,
-                       int zero_point, uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st);
+                       int zero_point, float clip_ratio, uint32_t* codes, float* scales, uint8_t* zeros,
+                       hipStream_t st);
 
 // ---- a6: W4A16 product
 struct GemmPlan {

@@ -7,6 +7,8 @@
 // (M = N*b/8 bytes); "009. AWQ Integration", Consequences (4-bit, two weights per byte) and
 // 关键设计 3 (the search scores the same quantizer that packing uses).
 //
+// With a clip ratio c (the configuration's optional min-max clipping, "009. AWQ Integration",
+// 关键设计 5) both ends of the range are multiplied by c before the step and the zero are formed.
 // The quantizer is evaluated in float64.  p = s*w is exact there (a float32 times a bf16 has at
 // most 32 significant bits), max/min are exact, and every division and rounding is a single
 // IEEE operation, so codes, steps and zeros are reproducible bit for bit by any float64
@@ -21,8 +23,9 @@ namespace awq {
 
 template <bool ZP>
 __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                              const float* __restrict__ s, int G, uint32_t* __restrict__ codes,
-                                              float* __restrict__ scales, uint8_t* __restrict__ zeros) {
+                                              const float* __restrict__ s, int G, double clip,
+                                              uint32_t* __restrict__ codes, float* __restrict__ scales,
+                                              uint8_t* __restrict__ zeros) {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t jg = blockIdx.y;
     if (n >= N) return;
@@ -37,6 +40,10 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
             am = fmax(am, fabs(pv));
         }
     }
+    // min-max clipping: both ends of the range scaled by the ratio (1: none), codes clamp below
+    mx *= clip;
+    mn *= clip;
+    am *= clip;
     float d;
     double z;
     if (ZP) {
@@ -66,12 +73,14 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
 }
 
 hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, int group_size,
-                       int zero_point, uint32_t* codes, float* scales, uint8_t* zeros, hipStream_t st) {
+                       int zero_point, float clip_ratio, uint32_t* codes, float* scales, uint8_t* zeros,
+                       hipStream_t st) {
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / group_size));
+    const double clip = clip_ratio > 0.f && clip_ratio < 1.f ? (double)clip_ratio : 1.0;
     if (zero_point)
-        k_pack<true><<<grid, 256, 0, st>>>(W, K, N, s, group_size, codes, scales, zeros);
+        k_pack<true><<<grid, 256, 0, st>>>(W, K, N, s, group_size, clip, codes, scales, zeros);
     else
-        k_pack<false><<<grid, 256, 0, st>>>(W, K, N, s, group_size, codes, scales, zeros);
+        k_pack<false><<<grid, 256, 0, st>>>(W, K, N, s, group_size, clip, codes, scales, zeros);
     return hipGetLastError();
 }
 

@@ -197,11 +197,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int G, int NA, int RBW, int NW, bool ZP>
+// CLIP: the quantizer's group range is clipped by the ratio clip_tab[i] of grid point i (both ends
+// scaled, codes clamped to the 16 levels); without it the range is the group's own.
+template <int G, int NA, int RBW, int NW, bool ZP, bool CLIP>
 __global__ __launch_bounds__(NW * 64, 1) void k_search(
     const u32x4* __restrict__ Xt, int T, int K, const floatx4* __restrict__ Wt, int NB,
-    const float* __restrict__ s_tab, const float* __restrict__ inv_tab, uint32_t stage_bytes, int n_grid, int n_asplit,
-    int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
+    const float* __restrict__ s_tab, const float* __restrict__ inv_tab, const float* __restrict__ clip_tab,
+    uint32_t stage_bytes, int n_grid, int n_asplit, int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
     constexpr int C = G / 32;            // K chunks per group
     constexpr int BM = NW * RBW * 16;    // token rows per workgroup
     constexpr int NWE = C * 128;         // 16-byte W entries of a group tile (float32)
@@ -302,6 +304,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // chunk: p = s*w, the group max/min (in registers, then across the 4 lanes of the column), the
     // step and zero, then per value: quantize, dequantize, subtract, unscale, round to bf16.
     const int slot = min(wave, NA - 1);
+    float crat = 1.f;   // clip ratio of this wavefront's grid point (CLIP only)
+    if constexpr (CLIP) crat = clip_tab[min(a0 + slot, n_grid - 1)];
     // E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].  The
     // level is rint(p/Delta) without the clamp to the code range: with Delta and the zero taken
     // from the group's own max and min, the level leaves the range only when p/Delta lies at a .5
@@ -364,27 +368,44 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         float d;
         if (ZP) {
             quad_max2(mx, nmn);
+            if constexpr (CLIP) {
+                mx *= crat;
+                nmn *= crat;
+            }
             d = (mx + nmn) * (1.0f / 15.0f);
         } else {
             mx = quad_max(mx);
+            if constexpr (CLIP) mx *= crat;
             d = mx * (1.0f / 7.0f);
         }
         // an all-zero group has d = 0 and every p = 0, so any finite reciprocal gives e = 0;
         // below FLT_MIN the step only meets values whose squares vanish in the loss
         d = fmaxf(d, 1.17549435e-38f);
         const float rd = __builtin_amdgcn_rcpf(d);
+        // clipped range: levels clamp to [-zero, 15 - zero] (zero = rne(-min/Delta)) or [-7, 7]
+        float llo = -7.f, lhi = 7.f;
+        if constexpr (CLIP && ZP) {
+            const float z = fminf(rintf(nmn * rd), 15.f);
+            llo = -z;
+            lhi = 15.f - z;
+        }
+        auto level = [&](float t) {
+            const float l = rintf(t);
+            if constexpr (CLIP) return __builtin_amdgcn_fmed3f(l, llo, lhi);
+            else return l;
+        };
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const float* v = &pk[c * 8];
             float e[8];   // (level*Delta - s*w) / s
-            e[0] = fmaf(rintf(v[0] * rd), d, -v[0]) * rowbcast<8>(sv[c]);
-            e[1] = fmaf(rintf(v[1] * rd), d, -v[1]) * rowbcast<9>(sv[c]);
-            e[2] = fmaf(rintf(v[2] * rd), d, -v[2]) * rowbcast<10>(sv[c]);
-            e[3] = fmaf(rintf(v[3] * rd), d, -v[3]) * rowbcast<11>(sv[c]);
-            e[4] = fmaf(rintf(v[4] * rd), d, -v[4]) * rowbcast<12>(sv[c]);
-            e[5] = fmaf(rintf(v[5] * rd), d, -v[5]) * rowbcast<13>(sv[c]);
-            e[6] = fmaf(rintf(v[6] * rd), d, -v[6]) * rowbcast<14>(sv[c]);
-            e[7] = fmaf(rintf(v[7] * rd), d, -v[7]) * rowbcast<15>(sv[c]);
+            e[0] = fmaf(level(v[0] * rd), d, -v[0]) * rowbcast<8>(sv[c]);
+            e[1] = fmaf(level(v[1] * rd), d, -v[1]) * rowbcast<9>(sv[c]);
+            e[2] = fmaf(level(v[2] * rd), d, -v[2]) * rowbcast<10>(sv[c]);
+            e[3] = fmaf(level(v[3] * rd), d, -v[3]) * rowbcast<11>(sv[c]);
+            e[4] = fmaf(level(v[4] * rd), d, -v[4]) * rowbcast<12>(sv[c]);
+            e[5] = fmaf(level(v[5] * rd), d, -v[5]) * rowbcast<13>(sv[c]);
+            e[6] = fmaf(level(v[6] * rd), d, -v[6]) * rowbcast<14>(sv[c]);
+            e[7] = fmaf(level(v[7] * rd), d, -v[7]) * rowbcast<15>(sv[c]);
             if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
                 Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                                                 pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
@@ -541,10 +562,11 @@ __global__ __launch_bounds__(256) void k_reduce_losses(const double* __restrict_
     if (threadIdx.x == 0) losses[i] = sm[0];
 }
 
-// best = first index of the minimum loss; s_best = s_tab[best].
+// best = first index of the minimum loss; row = table[best] (K values: the scale row s_best of the
+// alpha search; 1 value: the clip ratio of the clip search).
 __global__ __launch_bounds__(256) void k_select(const double* __restrict__ losses, int n_grid,
-                                                const float* __restrict__ s_tab, int64_t K,
-                                                int32_t* __restrict__ best, float* __restrict__ s_best) {
+                                                const float* __restrict__ table, int64_t K,
+                                                int32_t* __restrict__ best, float* __restrict__ row) {
     __shared__ int b;
     if (threadIdx.x == 0) {
         int bi = 0;
@@ -555,49 +577,74 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ losse
     }
     __syncthreads();
     for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < K; k += (int64_t)gridDim.x * 256)
-        s_best[k] = s_tab[(int64_t)b * K + k];
+        row[k] = table[(int64_t)b * K + k];
+}
+
+// Clip search: every grid row of the scale table is the fixed s (and its float32 reciprocal).
+__global__ __launch_bounds__(256) void k_fixed_scale_rows(const float* __restrict__ s, int64_t K,
+                                                          float* __restrict__ s_tab, float* __restrict__ inv_tab) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int j = blockIdx.y;
+    if (k >= K) return;
+    const float v = s[k];
+    s_tab[(int64_t)j * K + k] = v;
+    inv_tab[(int64_t)j * K + k] = 1.0f / v;
+}
+
+struct ClipRatios {
+    float c[kMaxGrid];
+};
+__global__ void k_write_clip(ClipRatios r, int n, float* __restrict__ tab) {
+    if ((int)threadIdx.x < n) tab[threadIdx.x] = r.c[threadIdx.x];
 }
 
 namespace {
 
-// Instantiations: (group size, zero point) x two tile shapes.  8 wavefronts (2 per SIMD), 7 alphas
-// per workgroup (21 = 3 slices of 7), and RBW row blocks of 16 per wavefront: RBW = 5 (640 token
-// rows, 140 accumulator VGPRs per lane) halves the E work per product against RBW = 4 (512 rows) by
-// a fifth; the plan takes it unless padding the tokens to 640-row tiles costs more than that.
+// Instantiations: (group size, zero point, clipping) x two tile shapes.  8 wavefronts (2 per SIMD),
+// 7 alphas (or clip ratios) per workgroup (21 = 3 slices of 7), and RBW row blocks of 16 per
+// wavefront: RBW = 5 (640 token rows, 140 accumulator VGPRs per lane) cuts the E work per product
+// by a fifth against RBW = 4 (512 rows); the plan takes it unless padding the tokens to 640-row
+// tiles costs more than that.
 constexpr int kNA = 7, kNW = 8;
 
-typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, uint32_t,
-                          int, int, int, int, double*);
+typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, const float*,
+                          uint32_t, int, int, int, int, double*);
 
-template <int RBW>
+template <int RBW, bool CLIP>
 search_fn pick_rbw(int g, int zp) {
     if (zp) {
-        if (g == 32) return k_search<32, kNA, RBW, kNW, true>;
-        if (g == 64) return k_search<64, kNA, RBW, kNW, true>;
-        if (g == 128) return k_search<128, kNA, RBW, kNW, true>;
+        if (g == 32) return k_search<32, kNA, RBW, kNW, true, CLIP>;
+        if (g == 64) return k_search<64, kNA, RBW, kNW, true, CLIP>;
+        if (g == 128) return k_search<128, kNA, RBW, kNW, true, CLIP>;
     } else {
-        if (g == 32) return k_search<32, kNA, RBW, kNW, false>;
-        if (g == 64) return k_search<64, kNA, RBW, kNW, false>;
-        if (g == 128) return k_search<128, kNA, RBW, kNW, false>;
+        if (g == 32) return k_search<32, kNA, RBW, kNW, false, CLIP>;
+        if (g == 64) return k_search<64, kNA, RBW, kNW, false, CLIP>;
+        if (g == 128) return k_search<128, kNA, RBW, kNW, false, CLIP>;
     }
     return nullptr;
 }
 
-search_fn pick(int g, int zp, int rbw) { return rbw == 5 ? pick_rbw<5>(g, zp) : pick_rbw<4>(g, zp); }
+search_fn pick(int g, int zp, int rbw, bool clip) {
+    if (clip) return rbw == 5 ? pick_rbw<5, true>(g, zp) : pick_rbw<4, true>(g, zp);
+    return rbw == 5 ? pick_rbw<5, false>(g, zp) : pick_rbw<4, false>(g, zp);
+}
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid) {
+SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero_point, int n_grid, bool clip) {
     SearchPlan p{};
     p.group_size = group_size;
     p.n_grid = n_grid;
     p.zero_point = zero_point;
     // rows per workgroup: 640 (RBW = 5) unless its padding of T exceeds 512-row tiles' by more than
-    // the ~4.5% it gains per row (measured on the 4096x4096 layer)
+    // the ~4.5% it gains per row (measured on the 4096x4096 layer); the clipped quantizer needs the
+    // registers of the 512-row tile.  The workspace holds either shape.
     const int64_t pad5 = (T + 639) / 640 * 640, pad4 = (T + 511) / 512 * 512;
-    p.variant = pad5 * 1000 <= pad4 * 1045 ? 5 : 4;   // row blocks per wavefront
+    p.variant = !clip && pad5 * 1000 <= pad4 * 1045 ? 5 : 4;   // row blocks per wavefront
+    const int64_t xt_rows = pad5 > pad4 ? pad5 : pad4;
+    const int64_t max_tb = (T + 511) / 512;
     p.na = kNA;
     p.bm = p.variant * kNW * 16;
     p.n_asplit = (n_grid + kNA - 1) / kNA;
@@ -610,24 +657,29 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     p.off_s = off;    off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_inv = off;  off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(float));
-    p.off_xt = off;   off = align256(off + (size_t)p.tb * p.bm * K * sizeof(uint16_t));
-    p.off_part = off; off = align256(off + (size_t)p.tb * p.nb * n_grid * sizeof(double));
+    p.off_xt = off;   off = align256(off + (size_t)xt_rows * K * sizeof(uint16_t));
+    p.off_part = off; off = align256(off + (size_t)max_tb * p.nb * n_grid * sizeof(double));
+    p.off_clip = off; off = align256(off + (size_t)n_grid * sizeof(float));
     p.ws_bytes = off;
     return p;
 }
 
-hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
-                         const float* mean_abs, const SearchPlan& p, void* ws, double* losses,
-                         int32_t* best, float* s_best, hipStream_t st) {
+namespace {
+
+// The common part of both searches once the scale table, its reciprocals and (when clipping) the
+// clip ratios of the grid are in the workspace: tile W and X, run the fused kernel, reduce the
+// partials and pick the first minimum.
+hipError_t run_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p,
+                      void* ws, bool clip, double* losses, int32_t* best, const float* sel_table, int64_t sel_len,
+                      float* sel_row, hipStream_t st) {
     char* base = (char*)ws;
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
     floatx4* Wt = (floatx4*)(base + p.off_wt);
     u32x4* Xt = (u32x4*)(base + p.off_xt);
     double* part = (double*)(base + p.off_part);
-
-    hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
-    if (e != hipSuccess) return e;
+    const float* clip_tab = (const float*)(base + p.off_clip);
+    hipError_t e;
     const int64_t total = p.nb * (K / 32) * 64;
     const unsigned tgrid = (unsigned)((total + 255) / 256);
     if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
@@ -640,17 +692,61 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     else if (p.group_size == 64) k_tile_x<64><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
     else k_tile_x<128><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    search_fn fn = pick(p.group_size, p.zero_point, p.variant);
+    search_fn fn = pick(p.group_size, p.zero_point, p.variant, clip);
     if (!fn) return hipErrorInvalidValue;
     const uint32_t stage_bytes = (uint32_t)(p.off_xt - p.off_s);   // scale table, reciprocals, W tiles
-    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, stage_bytes,
-                                             p.n_grid, p.n_asplit, (int)p.tiles, (int)p.tiles_per_xcd, part);
+    fn<<<(unsigned)p.grid, kNW * 64, 0, st>>>(Xt, (int)T, (int)K, Wt, (int)p.nb, s_tab, inv_tab, clip_tab,
+                                             stage_bytes, p.n_grid, p.n_asplit, (int)p.tiles, (int)p.tiles_per_xcd,
+                                             part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_reduce_losses<<<(unsigned)p.n_grid, 256, 0, st>>>(part, p.tb * p.nb, p.n_grid, losses);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_select<<<(unsigned)((K + 255) / 256 < 64 ? (K + 255) / 256 : 64), 256, 0, st>>>(losses, p.n_grid, s_tab,
-                                                                                     K, best, s_best);
+    const unsigned sgrid = (unsigned)((sel_len + 255) / 256 < 64 ? (sel_len + 255) / 256 : 64);
+    k_select<<<sgrid, 256, 0, st>>>(losses, p.n_grid, sel_table, sel_len, best, sel_row);
     return hipGetLastError();
+}
+
+hipError_t write_clip_table(const ClipRatios& r, int n, float* tab, hipStream_t st) {
+    k_write_clip<<<1, kMaxGrid, 0, st>>>(r, n, tab);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                         const float* mean_abs, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
+                         int32_t* best, float* s_best, hipStream_t st) {
+    char* base = (char*)ws;
+    float* s_tab = (float*)(base + p.off_s);
+    float* inv_tab = (float*)(base + p.off_inv);
+    hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
+    if (e != hipSuccess) return e;
+    const bool clip = clip_ratio > 0.f && clip_ratio < 1.f;
+    if (clip) {
+        ClipRatios r{};
+        for (int j = 0; j < p.n_grid; ++j) r.c[j] = clip_ratio;
+        if ((e = write_clip_table(r, p.n_grid, (float*)(base + p.off_clip), st)) != hipSuccess) return e;
+    }
+    return run_search(X, T, W, K, N, p, ws, clip, losses, best, s_tab, K, s_best, st);
+}
+
+hipError_t launch_clip_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                              const float* s, float clip_min, const SearchPlan& p, void* ws, double* losses,
+                              int32_t* best, float* clip_best, hipStream_t st) {
+    char* base = (char*)ws;
+    float* s_tab = (float*)(base + p.off_s);
+    float* inv_tab = (float*)(base + p.off_inv);
+    float* clip_tab = (float*)(base + p.off_clip);
+    dim3 grid((unsigned)((K + 255) / 256), (unsigned)p.n_grid);
+    k_fixed_scale_rows<<<grid, 256, 0, st>>>(s, K, s_tab, inv_tab);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // c_j = float32(1 - (1 - c_min) j / (n - 1)), evaluated in float64 in this order
+    ClipRatios r{};
+    const double cm = (double)clip_min;
+    for (int j = 0; j < p.n_grid; ++j) r.c[j] = (float)(1.0 - (1.0 - cm) * j / (p.n_grid - 1));
+    if ((e = write_clip_table(r, p.n_grid, clip_tab, st)) != hipSuccess) return e;
+    return run_search(X, T, W, K, N, p, ws, true, losses, best, clip_tab, 1, clip_best, st);
 }
 
 }  // namespace awq

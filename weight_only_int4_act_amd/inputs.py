@@ -90,8 +90,11 @@ def _silu(a):
 
 def small(T: int, K: int, N: int, seed: int = 0, group_size: int = 128,
           zero_point: bool = True, n_salient: Optional[int] = None,
-          salient_gain: float = 50.0, w_std: float = 0.02) -> Layer:
-    """c1-like draws at an arbitrary shape (for parity tests with ragged tails)."""
+          salient_gain: float = 50.0, w_std: float = 0.02, w_outlier_frac: float = 0.0,
+          w_outlier_gain: float = 10.0) -> Layer:
+    """c1-like draws at an arbitrary shape (for parity tests with ragged tails).  With
+    w_outlier_frac > 0, that fraction of the weights (drawn last) is multiplied by
+    w_outlier_gain, as in c4."""
     rng = np.random.default_rng(seed)
     W = _normal(rng, (K, N)) * np.float32(w_std)
     X = _normal(rng, (T, K))
@@ -99,6 +102,9 @@ def small(T: int, K: int, N: int, seed: int = 0, group_size: int = 128,
     if ns > 0:
         idx = rng.choice(K, ns, replace=False)
         X[:, idx] *= np.float32(salient_gain)
+    if w_outlier_frac > 0:
+        pos = rng.choice(K * N, max(1, int(round(w_outlier_frac * K * N))), replace=False)
+        W.reshape(-1)[pos] *= np.float32(w_outlier_gain)
     return Layer(f"small_{T}x{K}x{N}", to_bf16(X), to_bf16(W), group_size, zero_point)
 
 
