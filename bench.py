@@ -13,11 +13,13 @@ Also reported on the same JSON line:
   roofline      the search (dominant kernels) against the bf16 matrix-core peak; its duration
                 is measured with HIP events on the stream the library launches on;
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the same workload;
+  clip_search   the clip-ratio search on the same layer at the chosen s* (21 ratios 1 .. 0.5,
+                the same number of X.E products) against the bf16 matrix-core peak;
   gemv          the M = 1 W4A16 product over the seven linears of a 70B-shaped block
                 (462 MB of packed weights, rotated so the 256 MB Infinity Cache cannot hold
                 them) against HBM peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv] [--no-clip]
 """
 from __future__ import annotations
 
@@ -48,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--no-clip", action="store_true")
+    ap.add_argument("--clip-iters", type=int, default=5)
     ap.add_argument("--gemv-iters", type=int, default=50)
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns of the oracle's bounded sample (of 4096)")
@@ -209,6 +213,10 @@ def main():
         "best_alpha_index": int(best.item()),
     }
 
+    if not args.no_clip:
+        out["clip_search"] = bench_clip(A, torch, dev, X, W, s_best, g, layer.zero_point, ws_search, stream,
+                                        args.clip_iters)
+
     if not args.no_gemv:
         out["gemv"] = bench_gemv(A, I, torch, dev, args.gemv_iters)
 
@@ -217,6 +225,33 @@ def main():
         out["cpu_baseline"] = cpu_baseline(layer, args.cpu_cols)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_clip(A, torch, dev, X, W, s_best, g, zp, ws, stream, iters):
+    """The clip-ratio search on the same layer at the alpha search's s*: 21 ratios 1 .. 0.5, so the
+    X.E work equals the alpha search's (same fused kernel, clipped quantizer, 512-row tiles)."""
+    T, K = X.shape
+    N = W.shape[1]
+    cfg = A.qconfig(g, zp, 21)
+    losses = torch.empty(21, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    cbest = torch.empty(1, dtype=torch.float32, device=dev)
+    A.awq_clip_search(X, W, s_best, cfg, 0.5, ws, losses, best, cbest, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        A.awq_clip_search(X, W, s_best, cfg, 0.5, ws, losses, best, cbest, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 21 * 2.0 * T * K * N
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] clip search {ms:.3f} ms -> {tf:.1f} TFLOP/s, best ratio {float(cbest.item())}")
+    return {"workload": "c2 layer at s*: 21 clip ratios 1 .. 0.5", "ms": round(ms, 4), "achieved": round(tf, 3),
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "best_index": int(best.item()),
+            "best_ratio": float(cbest.item())}
 
 
 def bench_gemv(A, I, torch, dev, iters):
