@@ -84,10 +84,44 @@ def act_stats(X: np.ndarray, sum_abs: np.ndarray | None = None,
     return s, (s / n).astype(np.float32)
 
 
+def act_max(X: np.ndarray, max_abs: np.ndarray | None = None) -> np.ndarray:
+    """Per-input-channel statistic max_t |x_tk|, the alternative that [P1] 重要通道识别的统计依据
+    names next to the mean ("或 max").  ``max_abs`` (float32 [K]) accumulates it over
+    calibration batches.  float32 [K]; exact (the max of bf16 magnitudes)."""
+    m = np.abs(np.asarray(X, dtype=np.float64)).max(axis=0)
+    if max_abs is not None:
+        m = np.maximum(m, np.asarray(max_abs, dtype=np.float64))
+    return m.astype(np.float32)
+
+
+def weight_mean_abs(W: np.ndarray) -> np.ndarray:
+    """mean_j |W_kj| over the output columns of input channel k: the denominator of the closed
+    form of [P3] section 3.  Summed in float64, divided by N, rounded once to float32 [K]."""
+    W = np.asarray(W, dtype=np.float64)
+    return (np.abs(W).sum(axis=1) / W.shape[1]).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------- a2
 def alpha_grid(n_grid: int = 21) -> np.ndarray:
     """alpha_i = i/(n_grid-1): [P1] 缩放因子优化的完整流程 step 3, {0, 0.05, ..., 1.0}."""
     return np.arange(n_grid, dtype=np.float64) / float(n_grid - 1)
+
+
+def scale_table_ex(stat: np.ndarray, n_grid: int = 21, w_mean: np.ndarray | None = None,
+                   normalize: bool = False) -> np.ndarray:
+    """Variants of the scale family, each row rounded once to float32 from float64:
+    t[i, k] = max(stat_k, 1e-8) ** alpha_i, divided by max(w_mean_k, 1e-8) when ``w_mean`` is
+    given ([P3] section 3: s_i* = (E|X_i|)^alpha / mean_j |W_ij|), and divided by the row's
+    maximum when ``normalize`` ([P3] section Python 演示: the demo divides s by its maximum); stat is mean |x| or
+    max |x| ([P1] 重要通道识别的统计依据)."""
+    m = np.maximum(np.asarray(stat, dtype=np.float32).astype(np.float64), SCALE_FLOOR)
+    a = alpha_grid(n_grid)
+    t = m[None, :] ** a[:, None]
+    if w_mean is not None:
+        t = t / np.maximum(np.asarray(w_mean, dtype=np.float32).astype(np.float64), SCALE_FLOOR)[None, :]
+    if normalize:
+        t = t / t.max(axis=1, keepdims=True)
+    return t.astype(np.float32)
 
 
 def scale_table(mean_abs: np.ndarray, n_grid: int = 21) -> np.ndarray:
