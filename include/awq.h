@@ -98,6 +98,28 @@ int awq_act_stats(const void* X_bf16, int64_t T, int64_t K, double* sum_abs, int
                   int64_t total_tokens, float* mean_abs, void* workspace, size_t ws_bytes,
                   void* stream);
 
+/* ---------------------------------------------------------------- statistic and scale variants
+ * Per-input-channel max |x_tk| over the calibration tokens, the alternative statistic that
+ * [P1] 重要通道识别的统计依据 names next to the mean.  max_abs float32 [K] out (accumulate = 0)
+ * or in/out (accumulate = 1: the maximum with the values it holds).  Exact.
+ *   workspace >= awq_act_stats_workspace_size(T, K) bytes.
+ */
+int awq_act_max(const void* X_bf16, int64_t T, int64_t K, float* max_abs, int accumulate,
+                void* workspace, size_t ws_bytes, void* stream);
+/* mean_j |W_kj| over the output columns of each input channel: the denominator of the closed
+ * form s_i = (E|X_i|)^alpha / mean_j |W_ij| of [P3] section 3.  W bf16 [K, N]; w_mean float32
+ * [K] out (float64 sum, one division, one float32 rounding).
+ */
+int awq_weight_mean_abs(const void* W_bf16, int64_t K, int64_t N, float* w_mean, void* stream);
+/* Scale-table variants: s[i, k] = float32(t[i, k]) with, in float64,
+ *   t[i, k] = max(stat_k, 1e-8)^alpha_i  [ / max(w_mean_k, 1e-8) when w_mean is not NULL ]
+ *             [ / max_k t[i, k] when normalize = 1 ([P3] Python 演示: s / max(s)) ],
+ * alpha_i = i/(n_grid-1).  stat: mean |x| (awq_act_stats) or max |x| (awq_act_max).  With
+ * w_mean = NULL and normalize = 0 this is awq_scale_table.  s_table float32 [n_grid, K] out.
+ */
+int awq_scale_table_ex(const float* stat, const float* w_mean, int64_t K, int32_t n_grid,
+                       int32_t normalize, float* s_table, void* stream);
+
 /* ---------------------------------------------------------------- a2: scale table
  * s[i, k] = float32( max(m_k, 1e-8) ^ alpha_i ), alpha_i = i/(n_grid-1), evaluated in
  * float64 ([P1] 缩放因子优化的完整流程 step 3: s_j(alpha) = activation_scale[j]^alpha).
@@ -136,6 +158,16 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
  */
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg,
              uint32_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/* ---------------------------------------------------------------- search over a given table
+ * awq_search with the alpha grid's scale table replaced by the caller's: every row s_i of
+ * s_table (float32 [cfg->n_grid, K], device, positive finite values) is scored with the same
+ * loss, the first minimum wins and s_best = its row.  Use it with awq_scale_table_ex for the
+ * statistic and scale-family variants.  workspace >= awq_search_workspace_size(T, K, N, cfg).
+ */
+int awq_search_table(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N,
+                     const float* s_table, const awq_qconfig* cfg, void* workspace, size_t ws_bytes,
+                     double* losses, int32_t* best, float* s_best, void* stream);
 
 /* ---------------------------------------------------------------- clip search
  * The search of awq_search with the alpha grid replaced by a grid of clip ratios at fixed

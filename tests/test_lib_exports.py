@@ -87,6 +87,18 @@ def test_host_validation_rejects_before_launch(awq):
                                nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_clip_search(p, 8, p, 128, 16, p, ctypes.byref(cfg), ctypes.c_float(0.5), p, need - 1, p, p, p,
                                nul) == awq.AWQ_ERR_WORKSPACE
+    # statistic and scale variants, search over a given table
+    assert lib.awq_act_max(nul, 8, 16, p, 0, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_act_max(p, 8, 16, p, 3, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_act_max(p, 4096, 4096, p, 0, p, 8, nul) == awq.AWQ_ERR_WORKSPACE
+    assert lib.awq_weight_mean_abs(p, 0, 16, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_scale_table_ex(p, nul, 16, 1, 0, p, nul) == awq.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_scale_table_ex(p, nul, 16, 21, 2, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_scale_table_ex(nul, p, 16, 21, 0, p, nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search_table(p, 8, p, 128, 16, nul, ctypes.byref(cfg), p, ws, p, p, p,
+                                nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search_table(p, 8, p, 128, 16, p, ctypes.byref(cfg), p, need - 1, p, p, p,
+                                nul) == awq.AWQ_ERR_WORKSPACE
     # stats
     assert lib.awq_act_stats(p, 8, 16, nul, 0, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_act_stats(p, 8, 16, p, 0, 7, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG   # total < T

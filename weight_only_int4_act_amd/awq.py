@@ -55,6 +55,10 @@ _SIGNATURES = {
     "awq_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
     "awq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _CFG, _P, _P, _P, _P]),
     "awq_clip_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, ctypes.c_float, _P, _SZ, _P, _P, _P, _P]),
+    "awq_search_table": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
+    "awq_act_max": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
+    "awq_weight_mean_abs": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "awq_scale_table_ex": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P]),
     "awq_w4a16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "awq_w4a16_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -151,6 +155,35 @@ def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, codes: torch.Te
     K, N = W.shape
     _check("awq_pack", _lib.awq_pack(_ptr(W), K, N, _ptr(s), ctypes.byref(cfg), _ptr(codes), _ptr(scales),
                                      _ptr(zeros), _stream(stream)))
+
+
+def awq_act_max(X: torch.Tensor, max_abs: torch.Tensor, accumulate: bool, ws: torch.Tensor, stream=None) -> None:
+    T, K = X.shape
+    _check("awq_act_max", _lib.awq_act_max(_ptr(X), T, K, _ptr(max_abs), 1 if accumulate else 0, _ptr(ws),
+                                           _nbytes(ws), _stream(stream)))
+
+
+def awq_weight_mean_abs(W: torch.Tensor, w_mean: torch.Tensor, stream=None) -> None:
+    K, N = W.shape
+    _check("awq_weight_mean_abs", _lib.awq_weight_mean_abs(_ptr(W), K, N, _ptr(w_mean), _stream(stream)))
+
+
+def awq_scale_table_ex(stat: torch.Tensor, w_mean: Optional[torch.Tensor], n_grid: int, normalize: bool,
+                       s_table: torch.Tensor, stream=None) -> None:
+    _check("awq_scale_table_ex", _lib.awq_scale_table_ex(_ptr(stat), _ptr(w_mean) if w_mean is not None else None,
+                                                         stat.numel(), int(n_grid), 1 if normalize else 0,
+                                                         _ptr(s_table), _stream(stream)))
+
+
+def awq_search_table(X: torch.Tensor, W: torch.Tensor, s_table: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
+                     losses: torch.Tensor, best: torch.Tensor, s_best: torch.Tensor, stream=None) -> None:
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K or tuple(s_table.shape) != (cfg.n_grid, K):
+        raise ValueError(f"shapes: X [T, {K}], W [{K2}, N], s_table {tuple(s_table.shape)} (want [{cfg.n_grid}, {K}])")
+    _check("awq_search_table", _lib.awq_search_table(_ptr(X), T, _ptr(W), K, N, _ptr(s_table), ctypes.byref(cfg),
+                                                     _ptr(ws), _nbytes(ws), _ptr(losses), _ptr(best), _ptr(s_best),
+                                                     _stream(stream)))
 
 
 def awq_clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, clip_min: float,

@@ -57,6 +57,34 @@ int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_t
     return hip_status(awq::launch_scale_table(mean_abs, K, n_grid, s_table, nullptr, (hipStream_t)stream));
 }
 
+int awq_act_max(const void* X_bf16, int64_t T, int64_t K, float* max_abs, int accumulate, void* workspace,
+                size_t ws_bytes, void* stream) {
+    if (!X_bf16 || !max_abs || T <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (accumulate != 0 && accumulate != 1) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(X_bf16, 16) || !aligned(max_abs, 4)) return AWQ_ERR_INVALID_ARG;
+    const awq::StatsPlan p = awq::plan_stats(T, K);
+    if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_act_max((const uint16_t*)X_bf16, T, K, max_abs, accumulate, workspace, p,
+                                          (hipStream_t)stream));
+}
+
+int awq_weight_mean_abs(const void* W_bf16, int64_t K, int64_t N, float* w_mean, void* stream) {
+    if (!W_bf16 || !w_mean || K <= 0 || N <= 0 || K > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(W_bf16, 2) || !aligned(w_mean, 4)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_weight_mean_abs((const uint16_t*)W_bf16, K, N, w_mean, (hipStream_t)stream));
+}
+
+int awq_scale_table_ex(const float* stat, const float* w_mean, int64_t K, int32_t n_grid, int32_t normalize,
+                       float* s_table, void* stream) {
+    if (!stat || !s_table || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (n_grid < 2 || n_grid > 64) return AWQ_ERR_UNSUPPORTED;
+    if (normalize != 0 && normalize != 1) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(stat, 4) || !aligned(s_table, 4) || (w_mean && !aligned(w_mean, 4))) return AWQ_ERR_INVALID_ARG;
+    return hip_status(
+        awq::launch_scale_table_ex(stat, w_mean, K, n_grid, normalize, s_table, (hipStream_t)stream));
+}
+
 size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg) {
     if (T <= 0 || K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
     return awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid, false).ws_bytes;
@@ -99,6 +127,19 @@ int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int
     if (st != AWQ_OK) return st;
     return hip_status(awq::launch_search((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, mean_abs,
                                          cfg->clip_ratio, p, workspace, losses, best, s_best, (hipStream_t)stream));
+}
+
+int awq_search_table(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* s_table,
+                     const awq_qconfig* cfg, void* workspace, size_t ws_bytes, double* losses, int32_t* best,
+                     float* s_best, void* stream) {
+    awq::SearchPlan p;
+    const bool clip = cfg && cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f;
+    const int st =
+        check_search(X_bf16, T, W_bf16, K, N, s_table, cfg, workspace, ws_bytes, losses, best, s_best, clip, &p);
+    if (st != AWQ_OK) return st;
+    return hip_status(awq::launch_search_table((const uint16_t*)X_bf16, T, (const uint16_t*)W_bf16, K, N, s_table,
+                                               cfg->clip_ratio, p, workspace, losses, best, s_best,
+                                               (hipStream_t)stream));
 }
 
 int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N, const float* s,

@@ -20,9 +20,18 @@ hipError_t launch_stats(const uint16_t* X, int64_t T, int64_t K, double* sum_abs
                         int64_t total_tokens, float* mean_abs, double* partials, const StatsPlan& p,
                         hipStream_t st);
 
+// max |x| per channel (workspace: the statistic's partials; accumulate: max with the held values)
+hipError_t launch_act_max(const uint16_t* X, int64_t T, int64_t K, float* max_abs, int accumulate, void* ws,
+                          const StatsPlan& p, hipStream_t st);
+// mean_j |W_kj| per input channel
+hipError_t launch_weight_mean_abs(const uint16_t* W, int64_t K, int64_t N, float* w_mean, hipStream_t st);
+
 // ---- a2: scale table (and its reciprocal, used inside the search)
 hipError_t launch_scale_table(const float* mean_abs, int64_t K, int n_grid, float* s_tab, float* inv_tab,
                               hipStream_t st);
+// variants: optional mean |W| denominator and per-row normalization by the maximum
+hipError_t launch_scale_table_ex(const float* stat, const float* w_mean, int64_t K, int n_grid, int normalize,
+                                 float* s_tab, hipStream_t st);
 
 // ---- a3/a4: search
 struct SearchPlan {
@@ -45,6 +54,10 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
 hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
                          const float* mean_abs, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
                          int32_t* best, float* s_best, hipStream_t st);
+// the rows of a caller's scale table (n_grid x K, device) instead of the alpha grid
+hipError_t launch_search_table(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                               const float* table, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
+                               int32_t* best, float* s_best, hipStream_t st);
 // clip-ratio grid 1 .. clip_min at the fixed scales s
 hipError_t launch_clip_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
                               const float* s, float clip_min, const SearchPlan& p, void* ws, double* losses,

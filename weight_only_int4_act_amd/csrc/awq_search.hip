@@ -591,6 +591,17 @@ __global__ __launch_bounds__(256) void k_fixed_scale_rows(const float* __restric
     inv_tab[(int64_t)j * K + k] = 1.0f / v;
 }
 
+// A caller's table of candidate scale rows and their float32 reciprocals, into the workspace.
+__global__ __launch_bounds__(256) void k_table_rows(const float* __restrict__ table, int64_t K,
+                                                    float* __restrict__ s_tab, float* __restrict__ inv_tab) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int j = blockIdx.y;
+    if (k >= K) return;
+    const float v = table[(int64_t)j * K + k];
+    s_tab[(int64_t)j * K + k] = v;
+    inv_tab[(int64_t)j * K + k] = 1.0f / v;
+}
+
 struct ClipRatios {
     float c[kMaxGrid];
 };
@@ -720,6 +731,25 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
     hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
+    if (e != hipSuccess) return e;
+    const bool clip = clip_ratio > 0.f && clip_ratio < 1.f;
+    if (clip) {
+        ClipRatios r{};
+        for (int j = 0; j < p.n_grid; ++j) r.c[j] = clip_ratio;
+        if ((e = write_clip_table(r, p.n_grid, (float*)(base + p.off_clip), st)) != hipSuccess) return e;
+    }
+    return run_search(X, T, W, K, N, p, ws, clip, losses, best, s_tab, K, s_best, st);
+}
+
+hipError_t launch_search_table(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
+                               const float* table, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
+                               int32_t* best, float* s_best, hipStream_t st) {
+    char* base = (char*)ws;
+    float* s_tab = (float*)(base + p.off_s);
+    float* inv_tab = (float*)(base + p.off_inv);
+    dim3 grid((unsigned)((K + 255) / 256), (unsigned)p.n_grid);
+    k_table_rows<<<grid, 256, 0, st>>>(table, K, s_tab, inv_tab);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool clip = clip_ratio > 0.f && clip_ratio < 1.f;
     if (clip) {
