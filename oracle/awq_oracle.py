@@ -234,6 +234,17 @@ def losses(X: np.ndarray, W: np.ndarray, S: np.ndarray, group_size: int, zero_po
     return np.array([loss(X, W, S[i], group_size, zero_point, quantizer, clip) for i in range(S.shape[0])])
 
 
+def losses_multi(X: np.ndarray, Ws, S: np.ndarray, group_size: int, zero_point: bool,
+                 clip: float = 1.0):
+    """Joint search of several projections that read the same X and so must share one scale
+    vector (the 1/s division happens once, on X, before every projection; [P4] 关键设计 4 and
+    the fused ``attn.qkv`` layer of its usage).  The joint loss is the squared error over all
+    their outputs, L(alpha_i) = sum_j ||X (S_i^-1 Q(S_i W_j) - W_j)||^2 ([P1] step 4c per
+    projection).  Returns (joint [n_grid], each [n_w, n_grid])."""
+    each = np.array([losses(X, W, S, group_size, zero_point, clip=clip) for W in Ws])
+    return each.sum(axis=0), each
+
+
 def clip_grid(clip_min: float, n: int) -> np.ndarray:
     """Clip ratios c_j = fl32(1 - (1 - c_min) * j / (n - 1)), j = 0..n-1, in float64 before
     the rounding; c_0 = 1 (no clipping) comes first, so ties keep the unclipped quantizer."""
