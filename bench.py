@@ -15,11 +15,15 @@ Also reported on the same JSON line:
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the same workload;
   clip_search   the clip-ratio search on the same layer at the chosen s* (21 ratios 1 .. 0.5,
                 the same number of X.E products) against the bf16 matrix-core peak;
+  multi_search  the joint search of the q, k and v projections of a 70B-shaped block, which read
+                one X [4096, 8192] (W [8192, 8192 | 1024 | 1024]), against the three searches
+                run one by one and against the bf16 matrix-core peak;
   gemv          the M = 1 W4A16 product over the seven linears of a 70B-shaped block
                 (462 MB of packed weights, rotated so the 256 MB Infinity Cache cannot hold
                 them) against HBM peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv] [--no-clip]
+                    [--no-multi]
 """
 from __future__ import annotations
 
@@ -52,6 +56,8 @@ def parse():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-clip", action="store_true")
     ap.add_argument("--clip-iters", type=int, default=5)
+    ap.add_argument("--no-multi", action="store_true")
+    ap.add_argument("--multi-iters", type=int, default=3)
     ap.add_argument("--gemv-iters", type=int, default=50)
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns of the oracle's bounded sample (of 4096)")
@@ -217,6 +223,9 @@ def main():
         out["clip_search"] = bench_clip(A, torch, dev, X, W, s_best, g, layer.zero_point, ws_search, stream,
                                         args.clip_iters)
 
+    if not args.no_multi:
+        out["multi_search"] = bench_multi(A, I, torch, dev, args.multi_iters)
+
     if not args.no_gemv:
         out["gemv"] = bench_gemv(A, I, torch, dev, args.gemv_iters)
 
@@ -252,6 +261,56 @@ def bench_clip(A, torch, dev, X, W, s_best, g, zp, ws, stream, iters):
     return {"workload": "c2 layer at s*: 21 clip ratios 1 .. 0.5", "ms": round(ms, 4), "achieved": round(tf, 3),
             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "best_index": int(best.item()),
             "best_ratio": float(cbest.item())}
+
+
+def bench_multi(A, I, torch, dev, iters):
+    """Joint search of q, k and v (one X) against the three single searches, same inputs."""
+    log("[bench] multi: building X_attn [4096, 8192] and q, k, v")
+    X = I.c5_input(0, 0).to(dev)
+    Ws = [I.c5_weight(0, l).to(dev) for l in range(3)]
+    T, K = X.shape
+    Ns = [W.shape[1] for W in Ws]
+    cfg = A.qconfig(128, True, 21)
+    stream = torch.cuda.current_stream()
+    sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+    m = torch.empty(K, dtype=torch.float32, device=dev)
+    A.awq_act_stats(X, sum_abs, False, T, m, A.workspace(A.awq_act_stats_workspace_size(T, K), dev), stream)
+    ws = A.workspace(max([A.awq_search_multi_workspace_size(T, K, Ns, cfg)] +
+                         [A.awq_search_workspace_size(T, K, n, cfg) for n in Ns]), dev)
+    losses = torch.empty(21, dtype=torch.float64, device=dev)
+    each = torch.empty((3, 21), dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+
+    def joint():
+        A.awq_search_multi(X, Ws, m, cfg, ws, losses, each, best, s_best, stream)
+
+    def singles():
+        for W in Ws:
+            A.awq_search(X, W, m, cfg, ws, losses, best, s_best, stream)
+
+    res = {}
+    for name, fn in (("singles", singles), ("joint", joint)):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / iters
+    flops = 21 * 2.0 * T * K * sum(Ns)
+    tf = flops / (res["joint"] * 1e-3) / 1e12
+    log(f"[bench] multi search q,k,v: joint {res['joint']:.3f} ms ({tf:.1f} TFLOP/s), one by one "
+        f"{res['singles']:.3f} ms, alpha* {int(best.item())}")
+    return {"workload": "c5 attention: X [4096, 8192] shared by q, k, v; W [8192, 8192 | 1024 | 1024]; "
+                        "INT4 asym g=128, 21-point alpha grid",
+            "joint_ms": round(res["joint"], 4), "one_by_one_ms": round(res["singles"], 4),
+            "speedup": round(res["singles"] / res["joint"], 3), "achieved": round(tf, 3), "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_call": flops,
+            "best_index": int(best.item())}
 
 
 def bench_gemv(A, I, torch, dev, iters):

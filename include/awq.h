@@ -185,6 +185,29 @@ int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K
                     const float* s, const awq_qconfig* cfg, float clip_min, void* workspace,
                     size_t ws_bytes, double* losses, int32_t* best, float* clip_best, void* stream);
 
+/* ---------------------------------------------------------------- projections sharing X
+ * Projections that read the same activations (q, k and v; gate and up) share one scale vector
+ * once 1/s is applied to X a single time ([P4] 关键设计 4, the fused attn.qkv layer of its
+ * usage).  This search scores, for every alpha_i of awq_search's grid,
+ *   L_i = sum_j || X (S_i^-1 Q(S_i W_j) - W_j) ||^2,   j < n_w,
+ * the first minimum wins and s_best is its row; it equals awq_search on the matrix whose
+ * columns are all projections' columns, with each X tile loaded once for all of them.
+ *   X  bf16 [T, K] (device);  W_bf16  host array of n_w device pointers, W_j bf16 [K, N[j]];
+ *   N  host array of n_w column counts;  1 <= n_w <= AWQ_MAX_PROJECTIONS;
+ *   mean_abs float32 [K];  cfg as for awq_search (clip_ratio included).
+ *   losses  float64 [n_grid] out (joint);  losses_each  float64 [n_w, n_grid] out or NULL
+ *   (each projection's own L_i, reduced separately: they sum to the joint losses up to the
+ *   order of the float64 sums);  best  int32 [1] out;  s_best  float32 [K] out.
+ *   workspace >= awq_search_multi_workspace_size(T, K, n_w, N, cfg) bytes (0 for bad sizes).
+ * Each W_j is padded to a multiple of 16 columns with zeros, which quantize exactly.
+ */
+#define AWQ_MAX_PROJECTIONS 16
+size_t awq_search_multi_workspace_size(int64_t T, int64_t K, int32_t n_w, const int64_t* N,
+                                       const awq_qconfig* cfg);
+int awq_search_multi(const void* X_bf16, int64_t T, int32_t n_w, const void* const* W_bf16, const int64_t* N,
+                     int64_t K, const float* mean_abs, const awq_qconfig* cfg, void* workspace, size_t ws_bytes,
+                     double* losses, double* losses_each, int32_t* best, float* s_best, void* stream);
+
 /* ---------------------------------------------------------------- a6: W4A16 product
  * Y[m, n] = sum_k (x_mk / s_k) * (code_kn - zero_gn) * Delta_gn,  g = k / group_size
  * ([P1] 推理时的等效实现, 推理: Y = (X diag(1/s*)) Dequant(W_q), with the 1/s* scaling

@@ -99,6 +99,26 @@ def test_host_validation_rejects_before_launch(awq):
                                 nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_search_table(p, 8, p, 128, 16, p, ctypes.byref(cfg), p, need - 1, p, p, p,
                                 nul) == awq.AWQ_ERR_WORKSPACE
+    # projections sharing X: count, null or misaligned matrices, column counts, workspace
+    Ns = (ctypes.c_int64 * 3)(24, 8, 40)
+    Ws = (ctypes.c_void_p * 3)(256, 512, 768)
+    need_m = lib.awq_search_multi_workspace_size(8, 128, 3, Ns, ctypes.byref(cfg))
+    assert need_m == lib.awq_search_workspace_size(8, 128, 32 + 16 + 48, ctypes.byref(cfg))
+    assert lib.awq_search_multi_workspace_size(8, 128, 0, Ns, ctypes.byref(cfg)) == 0
+    assert lib.awq_search_multi_workspace_size(8, 128, awq.AWQ_MAX_PROJECTIONS + 1, Ns, ctypes.byref(cfg)) == 0
+    for n_w in (0, awq.AWQ_MAX_PROJECTIONS + 1):
+        assert lib.awq_search_multi(p, 8, n_w, Ws, Ns, 128, p, ctypes.byref(cfg), p, ws, p, nul, p, p,
+                                    nul) == awq.AWQ_ERR_INVALID_ARG
+    bad_w = (ctypes.c_void_p * 3)(256, 0, 768)
+    odd_w = (ctypes.c_void_p * 3)(256, 513, 768)
+    bad_n = (ctypes.c_int64 * 3)(24, 0, 40)
+    for W_, N_ in ((bad_w, Ns), (odd_w, Ns), (Ws, bad_n), (None, Ns), (Ws, None)):
+        assert lib.awq_search_multi(p, 8, 3, W_, N_, 128, p, ctypes.byref(cfg), p, ws, p, nul, p, p,
+                                    nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search_multi(p, 8, 3, Ws, Ns, 128, p, ctypes.byref(cfg), p, ws, p, ctypes.c_void_p(260), p, p,
+                                nul) == awq.AWQ_ERR_INVALID_ARG          # losses_each misaligned
+    assert lib.awq_search_multi(p, 8, 3, Ws, Ns, 128, p, ctypes.byref(cfg), p, need_m - 1, p, nul, p, p,
+                                nul) == awq.AWQ_ERR_WORKSPACE
     # stats
     assert lib.awq_act_stats(p, 8, 16, nul, 0, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_act_stats(p, 8, 16, p, 0, 7, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG   # total < T

@@ -22,6 +22,7 @@ AWQ_ERR_INVALID_ARG = -1
 AWQ_ERR_UNSUPPORTED = -2
 AWQ_ERR_WORKSPACE = -3
 AWQ_ERR_HIP = -4
+AWQ_MAX_PROJECTIONS = 16   # most matrices one awq_search_multi call takes
 
 
 class AwqError(RuntimeError):
@@ -56,6 +57,8 @@ _SIGNATURES = {
     "awq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _CFG, _P, _P, _P, _P]),
     "awq_clip_search": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, ctypes.c_float, _P, _SZ, _P, _P, _P, _P]),
     "awq_search_table": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
+    "awq_search_multi_workspace_size": (_SZ, [_I64, _I64, _I32, _P, _CFG]),
+    "awq_search_multi": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P, _P]),
     "awq_act_max": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
     "awq_weight_mean_abs": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "awq_scale_table_ex": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P]),
@@ -259,3 +262,56 @@ def gemm(X: torch.Tensor, q: Quantized, stream=None) -> torch.Tensor:
     ws = workspace(awq_w4a16_gemm_workspace_size(M, K, N, q.group_size), X.device)
     awq_w4a16_gemm(X, q.s, q.codes, q.scales, q.zeros, q.group_size, Y, ws, stream)
     return Y
+
+
+def _host_arrays(Ns, Ws=()):
+    n = len(Ns)
+    N = (ctypes.c_int64 * n)(*[int(v) for v in Ns])
+    P = (ctypes.c_void_p * n)(*[W.data_ptr() for W in Ws]) if Ws else None
+    return N, P
+
+
+def awq_search_multi_workspace_size(T: int, K: int, Ns, cfg: awq_qconfig) -> int:
+    N, _ = _host_arrays(Ns)
+    return int(_lib.awq_search_multi_workspace_size(T, K, len(Ns), N, ctypes.byref(cfg)))
+
+
+def awq_search_multi(X: torch.Tensor, Ws, mean_abs: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
+                     losses: torch.Tensor, losses_each: Optional[torch.Tensor], best: torch.Tensor,
+                     s_best: torch.Tensor, stream=None) -> None:
+    T, K = X.shape
+    for W in Ws:
+        if W.dim() != 2 or W.shape[0] != K:
+            raise ValueError(f"X is [T, {K}] but a projection is {tuple(W.shape)}")
+        _ptr(W)
+    N, P = _host_arrays([W.shape[1] for W in Ws], Ws)
+    _check("awq_search_multi", _lib.awq_search_multi(_ptr(X), T, len(Ws), P, N, K, _ptr(mean_abs),
+                                                     ctypes.byref(cfg), _ptr(ws), _nbytes(ws), _ptr(losses),
+                                                     _ptr(losses_each), _ptr(best), _ptr(s_best),
+                                                     _stream(stream)))
+
+
+def run_multi(X: torch.Tensor, Ws, cfg: awq_qconfig, stream=None) -> dict:
+    """Statistic of the shared X, one joint search over the projections Ws, and each projection
+    packed at the shared s*: the layers that read X are quantized with one scale vector."""
+    dev = X.device
+    T, K = X.shape
+    sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+    mean_abs = torch.empty(K, dtype=torch.float32, device=dev)
+    awq_act_stats(X, sum_abs, False, T, mean_abs, workspace(awq_act_stats_workspace_size(T, K), dev), stream)
+    ws = workspace(awq_search_multi_workspace_size(T, K, [W.shape[1] for W in Ws], cfg), dev)
+    losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=dev)
+    each = torch.empty((len(Ws), cfg.n_grid), dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    awq_search_multi(X, Ws, mean_abs, cfg, ws, losses, each, best, s_best, stream)
+    g = cfg.group_size
+    qs = []
+    for W in Ws:
+        N = W.shape[1]
+        codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+        scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+        zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+        awq_pack(W, s_best, cfg, codes, scales, zeros, stream)
+        qs.append(Quantized(codes, scales, zeros, s_best, g))
+    return {"mean_abs": mean_abs, "losses": losses, "each": each, "best": best, "s_best": s_best, "q": qs}

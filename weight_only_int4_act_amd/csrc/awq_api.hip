@@ -154,6 +154,39 @@ int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K
                                               clip_min, p, workspace, losses, best, clip_best, (hipStream_t)stream));
 }
 
+size_t awq_search_multi_workspace_size(int64_t T, int64_t K, int32_t n_w, const int64_t* N,
+                                      const awq_qconfig* cfg) {
+    if (n_w < 1 || n_w > AWQ_MAX_PROJECTIONS || !N) return 0;
+    int64_t cols = 0;
+    for (int j = 0; j < n_w; ++j) {
+        if (N[j] <= 0 || N[j] > kIntMax) return 0;
+        cols += (N[j] + 15) / 16 * 16;
+    }
+    if (T <= 0 || K <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
+    const bool clip = cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f;
+    return awq::plan_search(T, K, cols, cfg->group_size, cfg->zero_point, cfg->n_grid, clip).ws_bytes;
+}
+
+int awq_search_multi(const void* X_bf16, int64_t T, int32_t n_w, const void* const* W_bf16, const int64_t* N,
+                     int64_t K, const float* mean_abs, const awq_qconfig* cfg, void* workspace, size_t ws_bytes,
+                     double* losses, double* losses_each, int32_t* best, float* s_best, void* stream) {
+    if (n_w < 1 || n_w > AWQ_MAX_PROJECTIONS || !W_bf16 || !N) return AWQ_ERR_INVALID_ARG;
+    int64_t cols = 0;
+    for (int j = 0; j < n_w; ++j) {
+        if (!W_bf16[j] || !aligned(W_bf16[j], 2) || N[j] <= 0 || N[j] > kIntMax) return AWQ_ERR_INVALID_ARG;
+        cols += (N[j] + 15) / 16 * 16;
+    }
+    if (losses_each && !aligned(losses_each, 8)) return AWQ_ERR_INVALID_ARG;
+    awq::SearchPlan p;
+    const bool clip = cfg && cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f;
+    const int st =
+        check_search(X_bf16, T, W_bf16[0], K, cols, mean_abs, cfg, workspace, ws_bytes, losses, best, s_best, clip, &p);
+    if (st != AWQ_OK) return st;
+    return hip_status(awq::launch_search_multi((const uint16_t*)X_bf16, T, n_w, (const uint16_t* const*)W_bf16, N,
+                                               K, mean_abs, cfg->clip_ratio, p, workspace, losses, losses_each, best,
+                                               s_best, (hipStream_t)stream));
+}
+
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg, uint32_t* codes,
              float* scales, uint8_t* zeros, void* stream) {
     if (!W_bf16 || !s || !codes || !scales || !zeros || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;

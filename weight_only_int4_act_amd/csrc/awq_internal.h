@@ -58,6 +58,11 @@ hipError_t launch_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_
 hipError_t launch_search_table(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
                                const float* table, float clip_ratio, const SearchPlan& p, void* ws, double* losses,
                                int32_t* best, float* s_best, hipStream_t st);
+// several matrices sharing X (K rows each, N[j] columns, j < n_w), searched as one column-tile
+// stream (each padded to a multiple of 16 columns); plan for N = sum_j round_up(N[j], 16)
+hipError_t launch_search_multi(const uint16_t* X, int64_t T, int n_w, const uint16_t* const* W, const int64_t* N,
+                               int64_t K, const float* mean_abs, float clip_ratio, const SearchPlan& p, void* ws,
+                               double* losses, double* losses_each, int32_t* best, float* s_best, hipStream_t st);
 // clip-ratio grid 1 .. clip_min at the fixed scales s
 hipError_t launch_clip_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
                               const float* s, float clip_min, const SearchPlan& p, void* ws, double* losses,

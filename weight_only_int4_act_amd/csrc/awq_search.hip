@@ -562,6 +562,28 @@ __global__ __launch_bounds__(256) void k_reduce_losses(const double* __restrict_
     if (threadIdx.x == 0) losses[i] = sm[0];
 }
 
+// L_j[i] = sum over the token tiles and the column tiles [nb0, nb1) of partials[tile][i] (one
+// projection of a multi-matrix search): one workgroup per alpha, same fixed order as above.
+__global__ __launch_bounds__(256) void k_reduce_losses_range(const double* __restrict__ partials, int64_t tb,
+                                                             int64_t nb_total, int64_t nb0, int64_t nb1, int n_grid,
+                                                             double* __restrict__ losses) {
+    __shared__ double sm[256];
+    const int i = blockIdx.x;
+    const int64_t w = nb1 - nb0, tiles = tb * w;
+    double s = 0.0;
+    for (int64_t t = threadIdx.x; t < tiles; t += 256) {
+        const int64_t r = t / w, c = nb0 + t % w;
+        s += partials[(r * nb_total + c) * n_grid + i];
+    }
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) losses[i] = sm[0];
+}
+
 // best = first index of the minimum loss; row = table[best] (K values: the scale row s_best of the
 // alpha search; 1 value: the clip ratio of the clip search).
 __global__ __launch_bounds__(256) void k_select(const double* __restrict__ losses, int n_grid,
@@ -677,12 +699,24 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
 
 namespace {
 
-// The common part of both searches once the scale table, its reciprocals and (when clipping) the
-// clip ratios of the grid are in the workspace: tile W and X, run the fused kernel, reduce the
+// W [K, N] into the tiled float32 stream at column block nb0 (its padding columns are zero).
+hipError_t tile_w(const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p, void* ws, int64_t nb0,
+                  hipStream_t st) {
+    floatx4* Wt = (floatx4*)((char*)ws + p.off_wt) + nb0 * (K / 32) * 128;
+    const int64_t total = ((N + 15) / 16) * (K / 32) * 64;
+    const unsigned tgrid = (unsigned)((total + 255) / 256);
+    if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    return hipGetLastError();
+}
+
+// The common part of every search once the scale table, its reciprocals, (when clipping) the clip
+// ratios of the grid and the W tiles are in the workspace: tile X, run the fused kernel, reduce the
 // partials and pick the first minimum.
-hipError_t run_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p,
-                      void* ws, bool clip, double* losses, int32_t* best, const float* sel_table, int64_t sel_len,
-                      float* sel_row, hipStream_t st) {
+hipError_t run_search_tiled(const uint16_t* X, int64_t T, int64_t K, const SearchPlan& p, void* ws, bool clip,
+                            double* losses, int32_t* best, const float* sel_table, int64_t sel_len, float* sel_row,
+                            hipStream_t st) {
     char* base = (char*)ws;
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
@@ -691,12 +725,6 @@ hipError_t run_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K
     double* part = (double*)(base + p.off_part);
     const float* clip_tab = (const float*)(base + p.off_clip);
     hipError_t e;
-    const int64_t total = p.nb * (K / 32) * 64;
-    const unsigned tgrid = (unsigned)((total + 255) / 256);
-    if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
-    else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
-    else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t xtotal = p.tb * (p.bm / 16) * (K / 32) * 64;
     const unsigned xgrid = (unsigned)((xtotal + 255) / 256);
     if (p.group_size == 32) k_tile_x<32><<<xgrid, 256, 0, st>>>(X, T, K, xtotal, Xt);
@@ -715,6 +743,14 @@ hipError_t run_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K
     const unsigned sgrid = (unsigned)((sel_len + 255) / 256 < 64 ? (sel_len + 255) / 256 : 64);
     k_select<<<sgrid, 256, 0, st>>>(losses, p.n_grid, sel_table, sel_len, best, sel_row);
     return hipGetLastError();
+}
+
+hipError_t run_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p,
+                      void* ws, bool clip, double* losses, int32_t* best, const float* sel_table, int64_t sel_len,
+                      float* sel_row, hipStream_t st) {
+    hipError_t e = tile_w(W, K, N, p, ws, 0, st);
+    if (e != hipSuccess) return e;
+    return run_search_tiled(X, T, K, p, ws, clip, losses, best, sel_table, sel_len, sel_row, st);
 }
 
 hipError_t write_clip_table(const ClipRatios& r, int n, float* tab, hipStream_t st) {
@@ -758,6 +794,39 @@ hipError_t launch_search_table(const uint16_t* X, int64_t T, const uint16_t* W, 
         if ((e = write_clip_table(r, p.n_grid, (float*)(base + p.off_clip), st)) != hipSuccess) return e;
     }
     return run_search(X, T, W, K, N, p, ws, clip, losses, best, s_tab, K, s_best, st);
+}
+
+hipError_t launch_search_multi(const uint16_t* X, int64_t T, int n_w, const uint16_t* const* W, const int64_t* N,
+                               int64_t K, const float* mean_abs, float clip_ratio, const SearchPlan& p, void* ws,
+                               double* losses, double* losses_each, int32_t* best, float* s_best, hipStream_t st) {
+    char* base = (char*)ws;
+    float* s_tab = (float*)(base + p.off_s);
+    float* inv_tab = (float*)(base + p.off_inv);
+    hipError_t e = launch_scale_table(mean_abs, K, p.n_grid, s_tab, inv_tab, st);
+    if (e != hipSuccess) return e;
+    const bool clip = clip_ratio > 0.f && clip_ratio < 1.f;
+    if (clip) {
+        ClipRatios r{};
+        for (int j = 0; j < p.n_grid; ++j) r.c[j] = clip_ratio;
+        if ((e = write_clip_table(r, p.n_grid, (float*)(base + p.off_clip), st)) != hipSuccess) return e;
+    }
+    int64_t nb0 = 0;
+    for (int j = 0; j < n_w; ++j) {
+        if ((e = tile_w(W[j], K, N[j], p, ws, nb0, st)) != hipSuccess) return e;
+        nb0 += (N[j] + 15) / 16;
+    }
+    if ((e = run_search_tiled(X, T, K, p, ws, clip, losses, best, s_tab, K, s_best, st)) != hipSuccess) return e;
+    if (!losses_each) return hipSuccess;
+    const double* part = (const double*)(base + p.off_part);
+    nb0 = 0;
+    for (int j = 0; j < n_w; ++j) {
+        const int64_t nb1 = nb0 + (N[j] + 15) / 16;
+        k_reduce_losses_range<<<(unsigned)p.n_grid, 256, 0, st>>>(part, p.tb, p.nb, nb0, nb1, p.n_grid,
+                                                                 losses_each + (int64_t)j * p.n_grid);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        nb0 = nb1;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_clip_search(const uint16_t* X, int64_t T, const uint16_t* W, int64_t K, int64_t N,
