@@ -50,6 +50,13 @@ in the design notes of the repository):
   levels; c = 1 is the unclipped quantizer.  A clip search scores c_j = 1 - (1 - c_min)
   j/(n-1), j = 0..n-1, at fixed scales s with the same loss and takes the first minimum.
 
+* power-of-two greedy ([P4] 关键设计 1-3): candidates c_j = 2**(j - n//2), j = 0..n-1
+  (n = 20: 2**-10 .. 2**9, 1 among them), s starts at 1; for each group independently, each
+  pass visits its channels in ascending order and sets s_k to the candidate with the smallest
+  group error, keeping the current value unless another is strictly smaller (scanning the
+  candidates in ascending order); the group error is sum_n sum_{i in group} (m_i (What_in -
+  W_in))^2 with What from the packing quantizer and m_i = mean |x_i|.
+
 No function here is "parity unpinned": each is pinned by tests under
 ``tests/test_oracle_*.py`` against worked values, closed forms, invariants and
 brute force.
@@ -276,6 +283,74 @@ def search(X: np.ndarray, W: np.ndarray, mean_abs: np.ndarray, group_size: int,
     L = losses(X, W, S, group_size, zero_point)
     b = select(L)
     return {"S": S, "losses": L, "best": b, "s_best": S[b].copy()}
+
+
+def pow2_candidates(n: int = 20) -> np.ndarray:
+    """The candidate scales of the greedy search, 2**(j - n//2) for j = 0..n-1: powers of two
+    around 1 ([P4] 关键设计 1; the default count there is 20)."""
+    return np.array([2.0 ** (j - n // 2) for j in range(n)])
+
+
+def group_error(W_g: np.ndarray, m_g: np.ndarray, s_g: np.ndarray, zero_point: bool,
+                clip: float = 1.0) -> float:
+    """Activation-weighted reconstruction error of one quantization group ([P4] 关键设计 1):
+    W_g [g, N] are the group's rows of W, m_g [g] the mean |x| of its channels and s_g [g]
+    their scales; the group is quantized as packing quantizes it ([P4] 关键设计 3) and
+    sum_n sum_i (m_i (What_in - W_in))^2 is returned."""
+    W_g = np.asarray(W_g, dtype=np.float64)
+    s_g = np.asarray(s_g, dtype=np.float64)
+    g = W_g.shape[0]
+    codes, delta, zero = quantize_groups(s_g[:, None] * W_g, g, zero_point, clip)
+    What = dequantize(codes, delta, zero, g) / s_g[:, None]
+    E = np.asarray(m_g, dtype=np.float64)[:, None] * (What - W_g)
+    return float(np.sum(E * E))
+
+
+def greedy_search(W: np.ndarray, mean_abs: np.ndarray, group_size: int, zero_point: bool,
+                  n_cand: int = 20, passes: int = 3, trace: list | None = None):
+    """Per-group coordinate greedy over power-of-two scales ([P4] 关键设计 1-2; its cost
+    O(passes * K * n * N * g), Consequences).  Groups of input channels are independent because
+    each group's quantization sees only its own channels' scales.  Every channel starts at
+    s = 1; a pass visits the group's channels in ascending order and, for channel k, scores
+    every candidate with the group error (the other channels at their current scales), then
+    moves s_k to the best candidate only if its error is strictly below the current one (first
+    such candidate in ascending order on ties).  Three passes let a channel whose enlarged
+    weight became the group maximum be revisited.
+
+    Returns a dict: ``idx`` int [K] (s_k = pow2_candidates(n)[idx_k]), ``s`` float32 [K],
+    ``err_rtn`` and ``err`` float64 [K/g] (group errors at s = 1 and at the result).  With
+    ``trace`` a list, (group, pass, k, errors of every candidate, chosen index) is appended
+    per decision."""
+    W = np.asarray(W, dtype=np.float64)
+    m = np.asarray(mean_abs, dtype=np.float64)
+    K, N = W.shape
+    g = int(group_size)
+    cand = pow2_candidates(n_cand)
+    one = n_cand // 2
+    idx = np.full(K, one, dtype=np.int64)
+    err_rtn = np.zeros(K // g)
+    err = np.zeros(K // g)
+    for j in range(K // g):
+        rows = slice(j * g, (j + 1) * g)
+        Wg, mg = W[rows], m[rows]
+        err_rtn[j] = group_error(Wg, mg, np.ones(g), zero_point)
+        for p in range(passes):
+            for i in range(g):
+                k = j * g + i
+                e = np.zeros(n_cand)
+                for c in range(n_cand):
+                    sg = cand[idx[rows]]
+                    sg[i] = cand[c]
+                    e[c] = group_error(Wg, mg, sg, zero_point)
+                best = idx[k]
+                for c in range(n_cand):
+                    if e[c] < e[best]:
+                        best = c
+                idx[k] = best
+                if trace is not None:
+                    trace.append((j, p, k, e, best))
+        err[j] = group_error(Wg, mg, cand[idx[rows]], zero_point)
+    return {"idx": idx, "s": cand[idx].astype(np.float32), "err_rtn": err_rtn, "err": err}
 
 
 def relative_error(L: float, X: np.ndarray, W: np.ndarray) -> float:
