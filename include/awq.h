@@ -208,6 +208,32 @@ int awq_search_multi(const void* X_bf16, int64_t T, int32_t n_w, const void* con
                      int64_t K, const float* mean_abs, const awq_qconfig* cfg, void* workspace, size_t ws_bytes,
                      double* losses, double* losses_each, int32_t* best, float* s_best, void* stream);
 
+/* ---------------------------------------------------------------- power-of-two greedy
+ * The search of [P4] 关键设计 1-3: per-channel scales restricted to powers of two around 1,
+ * c_j = 2^(j - n_cand/2) for j < n_cand (n_cand = 20: 2^-10 .. 2^9), found by a coordinate
+ * greedy inside each group of input channels.  Every channel starts at s = 1; each of `passes`
+ * passes visits a group's channels in ascending order and moves s_k to the candidate with the
+ * smallest group error (the other channels at their current scales), keeping the current value
+ * unless another is strictly smaller (the first such candidate in ascending order on ties).
+ * The group error is sum_n sum_{i in group} (m_i (What_in - W_in))^2 with What the packing
+ * quantizer of cfg applied to s_i W_in, divided by s_i, and m = mean |x| (awq_act_stats).
+ *   W  bf16 [K, N];  mean_abs  float32 [K];  cfg: group size and zero point (clip_ratio must
+ *   be 0 or 1, else AWQ_ERR_UNSUPPORTED; n_grid is not used);  2 <= n_cand <=
+ *   AWQ_MAX_POW2_CANDIDATES;  1 <= passes <= 64 ([P4] uses 20 and 3).
+ *   s_best  float32 [K] out (powers of two);  err_rtn, err  float64 [K/g] out or NULL: each
+ *   group's error at s = 1 and at the result.
+ *   workspace >= awq_greedy_workspace_size(K, N, cfg, n_cand) bytes.
+ * Weights must be finite with |w| < 2^100; the error of each element is exact and only the
+ * float64 sums round, so the choices agree with a float64 evaluation except between candidates
+ * whose errors differ by about 1e-16 relative.  One launch per decision step (passes * g
+ * launches), each over all groups and output columns; no call allocates or synchronizes.
+ */
+#define AWQ_MAX_POW2_CANDIDATES 32
+size_t awq_greedy_workspace_size(int64_t K, int64_t N, const awq_qconfig* cfg, int32_t n_cand);
+int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mean_abs, const awq_qconfig* cfg,
+                      int32_t n_cand, int32_t passes, void* workspace, size_t ws_bytes, float* s_best,
+                      double* err_rtn, double* err, void* stream);
+
 /* ---------------------------------------------------------------- a6: W4A16 product
  * Y[m, n] = sum_k (x_mk / s_k) * (code_kn - zero_gn) * Delta_gn,  g = k / group_size
  * ([P1] 推理时的等效实现, 推理: Y = (X diag(1/s*)) Dequant(W_q), with the 1/s* scaling

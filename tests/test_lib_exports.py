@@ -119,6 +119,24 @@ def test_host_validation_rejects_before_launch(awq):
                                 nul) == awq.AWQ_ERR_INVALID_ARG          # losses_each misaligned
     assert lib.awq_search_multi(p, 8, 3, Ws, Ns, 128, p, ctypes.byref(cfg), p, need_m - 1, p, nul, p, p,
                                 nul) == awq.AWQ_ERR_WORKSPACE
+    # power-of-two greedy: candidate count, passes, clip ratio, sizes, workspace
+    need_g = lib.awq_greedy_workspace_size(256, 40, ctypes.byref(cfg), 20)
+    assert need_g > 0 and lib.awq_greedy_workspace_size(256, 40, ctypes.byref(cfg), 1) == 0
+    assert lib.awq_greedy_workspace_size(256, 40, ctypes.byref(cfg), awq.AWQ_MAX_POW2_CANDIDATES + 1) == 0
+    for n_cand, passes in ((1, 3), (awq.AWQ_MAX_POW2_CANDIDATES + 1, 3), (20, 0), (20, 65)):
+        assert lib.awq_greedy_search(p, 256, 40, p, ctypes.byref(cfg), n_cand, passes, p, ws, p, nul, nul,
+                                     nul) == awq.AWQ_ERR_INVALID_ARG
+    clipped = awq.qconfig(128, True, 21, clip_ratio=0.9)
+    assert lib.awq_greedy_search(p, 256, 40, p, ctypes.byref(clipped), 20, 3, p, ws, p, nul, nul,
+                                 nul) == awq.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_greedy_search(nul, 256, 40, p, ctypes.byref(cfg), 20, 3, p, ws, p, nul, nul,
+                                 nul) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_greedy_search(p, 200, 40, p, ctypes.byref(cfg), 20, 3, p, ws, p, nul, nul,
+                                 nul) == awq.AWQ_ERR_INVALID_ARG                      # K % g
+    assert lib.awq_greedy_search(p, 256, 40, p, ctypes.byref(cfg), 20, 3, p, ws, p, ctypes.c_void_p(260), nul,
+                                 nul) == awq.AWQ_ERR_INVALID_ARG                      # misaligned err_rtn
+    assert lib.awq_greedy_search(p, 256, 40, p, ctypes.byref(cfg), 20, 3, p, need_g - 1, p, nul, nul,
+                                 nul) == awq.AWQ_ERR_WORKSPACE
     # stats
     assert lib.awq_act_stats(p, 8, 16, nul, 0, 8, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG
     assert lib.awq_act_stats(p, 8, 16, p, 0, 7, p, p, ws, nul) == awq.AWQ_ERR_INVALID_ARG   # total < T

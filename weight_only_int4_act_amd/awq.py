@@ -22,6 +22,7 @@ AWQ_ERR_INVALID_ARG = -1
 AWQ_ERR_UNSUPPORTED = -2
 AWQ_ERR_WORKSPACE = -3
 AWQ_ERR_HIP = -4
+AWQ_MAX_POW2_CANDIDATES = 32   # most power-of-two candidates of awq_greedy_search
 AWQ_MAX_PROJECTIONS = 16   # most matrices one awq_search_multi call takes
 
 
@@ -59,6 +60,8 @@ _SIGNATURES = {
     "awq_search_table": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P]),
     "awq_search_multi_workspace_size": (_SZ, [_I64, _I64, _I32, _P, _CFG]),
     "awq_search_multi": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I64, _P, _CFG, _P, _SZ, _P, _P, _P, _P, _P]),
+    "awq_greedy_workspace_size": (_SZ, [_I64, _I64, _CFG, _I32]),
+    "awq_greedy_search": (ctypes.c_int, [_P, _I64, _I64, _P, _CFG, _I32, _I32, _P, _SZ, _P, _P, _P, _P]),
     "awq_act_max": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
     "awq_weight_mean_abs": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "awq_scale_table_ex": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P]),
@@ -315,3 +318,39 @@ def run_multi(X: torch.Tensor, Ws, cfg: awq_qconfig, stream=None) -> dict:
         awq_pack(W, s_best, cfg, codes, scales, zeros, stream)
         qs.append(Quantized(codes, scales, zeros, s_best, g))
     return {"mean_abs": mean_abs, "losses": losses, "each": each, "best": best, "s_best": s_best, "q": qs}
+
+
+def awq_greedy_workspace_size(K: int, N: int, cfg: awq_qconfig, n_cand: int = 20) -> int:
+    return int(_lib.awq_greedy_workspace_size(K, N, ctypes.byref(cfg), int(n_cand)))
+
+
+def awq_greedy_search(W: torch.Tensor, mean_abs: torch.Tensor, cfg: awq_qconfig, n_cand: int, passes: int,
+                      ws: torch.Tensor, s_best: torch.Tensor, err_rtn: Optional[torch.Tensor] = None,
+                      err: Optional[torch.Tensor] = None, stream=None) -> None:
+    K, N = W.shape
+    _check("awq_greedy_search", _lib.awq_greedy_search(_ptr(W), K, N, _ptr(mean_abs), ctypes.byref(cfg), int(n_cand),
+                                                       int(passes), _ptr(ws), _nbytes(ws), _ptr(s_best),
+                                                       _ptr(err_rtn), _ptr(err), _stream(stream)))
+
+
+def run_greedy(X: torch.Tensor, W: torch.Tensor, cfg: awq_qconfig, n_cand: int = 20, passes: int = 3,
+               stream=None) -> dict:
+    """Statistic of X, the power-of-two greedy over W's scales, and W packed at the result."""
+    dev = X.device
+    T, K = X.shape
+    N = W.shape[1]
+    sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+    mean_abs = torch.empty(K, dtype=torch.float32, device=dev)
+    awq_act_stats(X, sum_abs, False, T, mean_abs, workspace(awq_act_stats_workspace_size(T, K), dev), stream)
+    ws = workspace(awq_greedy_workspace_size(K, N, cfg, n_cand), dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    err_rtn = torch.empty(K // cfg.group_size, dtype=torch.float64, device=dev)
+    err = torch.empty_like(err_rtn)
+    awq_greedy_search(W, mean_abs, cfg, n_cand, passes, ws, s_best, err_rtn, err, stream)
+    g = cfg.group_size
+    codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+    zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+    awq_pack(W, s_best, cfg, codes, scales, zeros, stream)
+    return {"mean_abs": mean_abs, "s_best": s_best, "err_rtn": err_rtn, "err": err,
+            "q": Quantized(codes, scales, zeros, s_best, g)}

@@ -25,7 +25,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["awq_api.hip", "awq_stats.hip", "awq_search.hip", "awq_pack.hip", "awq_gemm.hip"]
+SOURCES = ["awq_api.hip", "awq_stats.hip", "awq_search.hip", "awq_pack.hip", "awq_gemm.hip", "awq_greedy.hip"]
 
 
 def hipcc() -> str:

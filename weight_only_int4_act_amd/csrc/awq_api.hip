@@ -187,6 +187,30 @@ int awq_search_multi(const void* X_bf16, int64_t T, int32_t n_w, const void* con
                                                s_best, (hipStream_t)stream));
 }
 
+size_t awq_greedy_workspace_size(int64_t K, int64_t N, const awq_qconfig* cfg, int32_t n_cand) {
+    if (K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK || n_cand < 2 || n_cand > AWQ_MAX_POW2_CANDIDATES) return 0;
+    return awq::plan_greedy(K, N, cfg->group_size, n_cand).ws_bytes;
+}
+
+int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mean_abs, const awq_qconfig* cfg,
+                      int32_t n_cand, int32_t passes, void* workspace, size_t ws_bytes, float* s_best,
+                      double* err_rtn, double* err, void* stream) {
+    if (!W_bf16 || !mean_abs || !s_best || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;
+    int st = check_cfg(cfg, K);
+    if (st != AWQ_OK) return st;
+    if (cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f) return AWQ_ERR_UNSUPPORTED;
+    if (n_cand < 2 || n_cand > AWQ_MAX_POW2_CANDIDATES || passes < 1 || passes > 64) return AWQ_ERR_INVALID_ARG;
+    if (K / cfg->group_size > 65535 || N > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (!aligned(W_bf16, 2) || !aligned(mean_abs, 4) || !aligned(s_best, 4) || (err_rtn && !aligned(err_rtn, 8)) ||
+        (err && !aligned(err, 8)))
+        return AWQ_ERR_INVALID_ARG;
+    const awq::GreedyPlan p = awq::plan_greedy(K, N, cfg->group_size, n_cand);
+    if (ws_bytes < p.ws_bytes || !workspace) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_greedy((const uint16_t*)W_bf16, K, N, mean_abs, cfg->zero_point, passes, p,
+                                         workspace, s_best, err_rtn, err, (hipStream_t)stream));
+}
+
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg, uint32_t* codes,
              float* scales, uint8_t* zeros, void* stream) {
     if (!W_bf16 || !s || !codes || !scales || !zeros || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;

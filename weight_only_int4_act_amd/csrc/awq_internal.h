@@ -73,6 +73,17 @@ hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, 
                        int zero_point, float clip_ratio, uint32_t* codes, float* scales, uint8_t* zeros,
                        hipStream_t st);
 
+// ---- power-of-two greedy over the per-channel scales
+struct GreedyPlan {
+    int group_size, n_cand;
+    int64_t groups, n_slices, part_stride;
+    size_t off_idx, off_part, off_rtn, ws_bytes;
+};
+GreedyPlan plan_greedy(int64_t K, int64_t N, int group_size, int n_cand);
+hipError_t launch_greedy(const uint16_t* W, int64_t K, int64_t N, const float* mean_abs, int zero_point,
+                         int passes, const GreedyPlan& p, void* ws, float* s_best, double* err_rtn, double* err,
+                         hipStream_t st);
+
 // ---- a6: W4A16 product
 struct GemmPlan {
     int variant;             // 0: M = 1 GEMV; else row blocks of 16 per wavefront (1, 2 or 4)
