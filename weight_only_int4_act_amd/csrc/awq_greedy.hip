@@ -14,17 +14,25 @@
 // the decision redundantly (every workgroup of a group reaches the same one), so no workgroup ever
 // waits on another.
 //
-// Exactness.  With power-of-two scales p = s*w is exact in float32, and the packing quantizer's
-// code, rne(p/Delta) evaluated in float64, equals the exactly rounded quotient: p carries 8
-// significant bits and Delta 24, so a quotient that is not exactly a half-integer stays more than
-// 2^-25 away from one, far beyond float64's error.  The kernel forms p/Delta with a float32
-// reciprocal (error below 3e-6 for the |p/Delta| <= 15 that occur) and settles the rare quotient
-// within 2^-17 of a half-integer with an exact float64 residual.  The weighted error of an element,
-// m (What - w) = (m/s) (level*Delta - p), is exact as well: level*Delta - p is a multiple of
-// Delta's last bit and at most Delta/2 in size, so one fused multiply-add gives it exactly in
-// float32, and the product with m/s is exact in float64.  Only the float64 sums of squares round,
-// so every decision matches any float64 evaluation of the definition except on differences of
-// order 1e-16 between candidates.
+// Exactness.  With power-of-two scales p = s*w is a bf16 value (8 significant bits) and Delta a
+// float32 (24), so p/Delta is either exactly a half-integer or more than 2^-25 away from one.
+// The kernel forms the quotient as p * r, r within two ulps of 1/Delta (error below 2^-45), so
+// its nearest integer is the packing quantizer's code except at exact half-integers, where either
+// neighbour gives the same squared error (the two errors are +-Delta/2, and at the ends of the
+// range both clamp to the same level).  The zero point, which does change the codes, settles its
+// exact half-integers with an exact residual.  The weighted error of an element, m (What - w) = (m/s) (level*Delta
+// - p), is exact: level*Delta - p is a multiple of Delta's last bit no larger than Delta/2, and
+// its product with m/s needs at most 48 bits.  Only the float64 sums of squares round, so every
+// decision matches a float64 evaluation of the definition except between candidates whose errors
+// differ by about 1e-16 relative.
+//
+// Work.  A candidate that keeps the channel's scaled weight inside the range of the other
+// channels leaves the group's step and zero unchanged: its error is the others' error at the base
+// configuration plus its own element.  Only candidates that stretch the range need the whole
+// group again, and those are the largest ones (|c w| grows with c).  Each wavefront therefore
+// evaluates the others' error for the base configuration and for the top S candidates, S the most
+// any of its lanes needs, one configuration per pass over the column; the rest cost one element
+// each.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -34,50 +42,55 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Exact round-half-even of p / d for the quantizer's quotients (|p/d| <= 15.0001); r = 1/d with
-// at most 1 ulp of error.
-__device__ __forceinline__ float rne_quot(float p, float d, float r) {
-    const float q = p * r;
-    const float fl = floorf(q);
-    float n = rintf(q);
-    if (fabsf(q - fl - 0.5f) <= 0x1p-17f) {
-        const double diff = (double)p - ((double)fl + 0.5) * (double)d;   // exact in float64
-        n = diff > 0.0 ? fl + 1.f : diff < 0.0 ? fl : ((((int)fl) & 1) ? fl + 1.f : fl);
-    }
-    return n;
-}
-
-// Quantizer configuration of one (column, group) from the group range.
+// Quantizer configuration of one (column, group), float64: step, its reciprocal, and the
+// clamp bounds of the level (code - zero).
 struct Cfg {
-    float d, r, z;   // Delta, 1/Delta, zero point (0 in symmetric mode)
+    double d, r, lo, hi;
 };
+
+// 1/d to within an ulp or two: hardware estimate plus two Newton steps.  That is ample for the
+// quotients here, which sit either exactly on a half-integer or more than 2^-25 from one.
+__device__ __forceinline__ double recip(double d) {
+    double r = __builtin_amdgcn_rcp(d);
+    r = fma(fma(-d, r, 1.0), r, r);
+    return fma(fma(-d, r, 1.0), r, r);
+}
 
 template <bool ZP>
 __device__ __forceinline__ Cfg make_cfg(float hi, float lo) {
     Cfg c;
     if (ZP) {
-        float d = (float)(((double)hi - (double)lo) / 15.0);
+        float d = (float)(((double)hi - (double)lo) / 15.0);   // the step exactly as packing forms it
         if (d == 0.f) d = 1.f;
         c.d = d;
-        c.z = (float)fmin(fmax(rint(-(double)lo / (double)d), 0.0), 15.0);
+        c.r = recip(c.d);
+        // zero = rne(-lo/d): the product with r rounds to the right integer except on an exact
+        // half-integer, which the exact residual zf*d + lo = (zf - (-lo/d)) d = +-d/2 reveals
+        double zf = rint(-(double)lo * c.r);
+        const double res = fma(zf, c.d, (double)lo);
+        if (fabs(res) == 0.5 * c.d && (((int)zf) & 1)) zf += res > 0.0 ? -1.0 : 1.0;
+        const double z = fmin(fmax(zf, 0.0), 15.0);
+        c.lo = -z;
+        c.hi = 15.0 - z;
     } else {
         float d = (float)((double)hi / 7.0);   // hi = max |p|
         if (d == 0.f) d = 1.f;
         c.d = d;
-        c.z = 0.f;
+        c.r = recip(c.d);
+        c.lo = -7.0;
+        c.hi = 7.0;
     }
-    c.r = __builtin_amdgcn_rcpf(c.d);
     return c;
 }
 
-// (m/s)^2 (level*Delta - p)^2 for one element; ms = m/s.
+// acc + (ms (level*Delta - p))^2 for one element; ms = m/s.  In symmetric mode |p| <= max|p|
+// = 7 Delta (1 + 2^-24) keeps every level inside -7..7, so only the asymmetric form clamps.
 template <bool ZP>
-__device__ __forceinline__ double elem_err(float p, float ms, const Cfg& c) {
-    const float n = rne_quot(p, c.d, c.r);
-    const float lv = ZP ? __builtin_amdgcn_fmed3f(n + c.z, 0.f, 15.f) - c.z : __builtin_amdgcn_fmed3f(n, -7.f, 7.f);
-    const float es = fmaf(lv, c.d, -p);
-    const double t = (double)ms * (double)es;
-    return t * t;
+__device__ __forceinline__ double elem_acc(double p, double ms, const Cfg& c, double acc) {
+    double lv = rint(p * c.r);
+    if (ZP) lv = fmin(fmax(lv, c.lo), c.hi);
+    const double t = ms * fma(lv, c.d, -p);
+    return fma(t, t, acc);
 }
 
 // The decision of one step for one group, taken from the previous launch's partials:
@@ -117,25 +130,38 @@ __global__ __launch_bounds__(256) void k_greedy_init(int32_t* __restrict__ idx, 
     if (k < K) idx[k] = one;
 }
 
-// One decision step for every group.  Grid (n_slices, K/G), 256 threads, thread = output column.
+// One decision step for every group.  Grid (n_slices, K/G), 256 threads.  The G channels of an
+// output column are split over P = G/32 lanes of one wavefront (lane = part * 64/P + column), so
+// every thread holds 32 scaled weights; a wavefront covers 64/P columns and a workgroup 256/P.
 // step = pass * G + i scores channel i of each group; partials of step t go to part[t & 1].
 template <int G, bool ZP>
-__global__ __launch_bounds__(256, 2) void k_greedy_step(const uint16_t* __restrict__ W, int64_t N,
-                                                     const float* __restrict__ m, int32_t* __restrict__ idx,
-                                                     double* __restrict__ part, int64_t part_stride, int n_slices,
-                                                     int n_cand, int step, double* __restrict__ err_rtn) {
-    __shared__ double sm_chunk[8 * 32];
-    __shared__ double sm_sum[32];
-    __shared__ double sm_wave[4][32];
-    __shared__ float s_scale[G];   // s_j of the group's channels
-    __shared__ float s_ms[G];      // m_j / s_j
+__global__ __launch_bounds__(256) void k_greedy_step(const uint16_t* __restrict__ W, int64_t N,
+                                                  const float* __restrict__ m, int32_t* __restrict__ idx,
+                                                  double* __restrict__ part, int64_t part_stride, int n_slices,
+                                                  int n_cand, int step, double* __restrict__ err_rtn) {
+    constexpr int CH = 32, P = G / CH, CPW = kWave / P;   // channels per thread, parts, columns/wave
+    // one block so that m_j/s_j sits at LDS offset 0: the per-channel reads then fit the
+    // immediate offsets of paired 64-bit LDS reads from a single base register
+    __shared__ struct {
+        double ms[P * (CH + 1)];   // m_j / s_j (0 for the channel being decided), padded per part
+        double chunk[8 * 32];
+        double sum[32];
+        double wave[4][32];
+        float scale[G];            // s_j of the group's channels
+        int idx[G];
+    } sh;
+    double* const s_ms = sh.ms;
+    double* const sm_chunk = sh.chunk;
+    double* const sm_sum = sh.sum;
+    double (*const sm_wave)[32] = sh.wave;
+    float* const s_scale = sh.scale;
+    int* const s_idx = sh.idx;
     const int tid = threadIdx.x;
     const int grp = blockIdx.y, slice = blockIdx.x;
     const int64_t k0 = (int64_t)grp * G;
     const int one = n_cand / 2;
     const int i = step % G;
 
-    __shared__ int s_idx[G];
     for (int j = tid; j < G; j += kThreads) s_idx[j] = idx[k0 + j];
     __syncthreads();
     if (step > 0) {
@@ -156,27 +182,31 @@ __global__ __launch_bounds__(256, 2) void k_greedy_step(const uint16_t* __restri
     for (int j = tid; j < G; j += kThreads) {
         const float s = ldexpf(1.f, s_idx[j] - one);
         s_scale[j] = s;
-        s_ms[j] = m[k0 + j] / s;   // exact: division by a power of two
+        s_ms[(j / CH) * (CH + 1) + j % CH] = j == i ? 0.0 : (double)(m[k0 + j] / s);   // exact
     }
     __syncthreads();
 
-    // this thread's column of the group, scaled: p_j = s_j w_j.  A bf16 times a power of two is
-    // again a bf16 value, so the scaled column is kept as packed bf16 pairs (G/2 registers).
-    const int64_t n = (int64_t)slice * kThreads + tid;
-    uint32_t pk[G / 2];
+    const int wave = tid >> 6, lane = tid & 63;
+    const int prt = lane / CPW;                          // which CH channels of the column
+    const int64_t n = (int64_t)slice * (kThreads / P) + wave * CPW + lane % CPW;
+    const int j0 = prt * CH;
+    const double* ms_p = s_ms + prt * (CH + 1);
+    // This thread's channels of the column, scaled: p_j = s_j w_j (exact), with p_i = 0 (channel i
+    // is the one being decided; zero changes no range and, weighted by 0, adds no error).
+    uint32_t pk[CH / 2];
 #pragma unroll
-    for (int j = 0; j < G; j += 2) {
-        const float a = n < N ? bf16_lo((uint32_t)W[(k0 + j) * N + n]) * s_scale[j] : 0.f;
-        const float b = n < N ? bf16_lo((uint32_t)W[(k0 + j + 1) * N + n]) * s_scale[j + 1] : 0.f;
+    for (int j = 0; j < CH; j += 2) {
+        float a = n < N ? bf16_lo((uint32_t)W[(k0 + j0 + j) * N + n]) * s_scale[j0 + j] : 0.f;
+        float b = n < N ? bf16_lo((uint32_t)W[(k0 + j0 + j + 1) * N + n]) * s_scale[j0 + j + 1] : 0.f;
+        a = j0 + j == i ? 0.f : a;
+        b = j0 + j + 1 == i ? 0.f : b;
         pk[j / 2] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
     }
     auto pj = [&](int j) { return (j & 1) ? bf16_hi(pk[j >> 1]) : bf16_lo(pk[j >> 1]); };
     const float wi = n < N ? bf16_lo((uint32_t)W[(k0 + i) * N + n]) : 0.f;
-    // range of the other channels
-    float hiO = 0.f, loO = 0.f;
+    float hiO = 0.f, loO = 0.f;   // range of the other channels (0 included), over all parts
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        if (j == i) continue;
+    for (int j = 0; j < CH; ++j) {
         if (ZP) {
             hiO = fmaxf(hiO, pj(j));
             loO = fminf(loO, pj(j));
@@ -184,41 +214,60 @@ __global__ __launch_bounds__(256, 2) void k_greedy_step(const uint16_t* __restri
             hiO = fmaxf(hiO, fabsf(pj(j)));
         }
     }
-    const Cfg c0 = make_cfg<ZP>(hiO, loO);
-    double e0 = 0.0;
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-        if (j != i) e0 += elem_err<ZP>(pj(j), s_ms[j], c0);
-
+    for (int off = CPW; off < kWave; off <<= 1) {
+        hiO = fmaxf(hiO, __shfl_xor(hiO, off, kWave));
+        if (ZP) loO = fminf(loO, __shfl_xor(loO, off, kWave));
+    }
+    const bool owner = prt == i / CH;   // the lane of the column that adds channel i's own error
     const float mi = m[k0 + i];
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int c = 0; c < n_cand; ++c) {
-        // m_j / s_j are re-read from LDS on every candidate rather than held in G registers
-        asm volatile("" ::: "memory");
+    // the candidate's own element (weighted only on the lane that owns channel i) and the
+    // configuration it implies
+    auto own = [&](int c, float& pc, double& msc) {
         const float sc = ldexpf(1.f, c - one);
-        const float pc = wi * sc;
-        const float msc = mi / sc;
-        float hi, lo;
-        if (ZP) {
-            hi = fmaxf(hiO, pc);
-            lo = fminf(loO, pc);
-        } else {
-            hi = fmaxf(hiO, fabsf(pc));
-            lo = 0.f;
-        }
-        const Cfg cc = make_cfg<ZP>(hi, lo);
-        double acc;
-        if (cc.d == c0.d && cc.z == c0.z) {
-            acc = e0 + elem_err<ZP>(pc, msc, c0);
-        } else {
-            acc = 0.0;
+        pc = wi * sc;
+        msc = owner ? (double)(mi / sc) : 0.0;
+    };
+    auto own_cfg = [&](int c, float& pc, double& msc) {
+        own(c, pc, msc);
+        return ZP ? make_cfg<ZP>(fmaxf(hiO, pc), fminf(loO, pc)) : make_cfg<ZP>(fmaxf(hiO, fabsf(pc)), 0.f);
+    };
+    int need = 0;   // candidates (from the top) that stretch this column's range
+    for (int c = 0; c < n_cand; ++c) {
+        const float pc = wi * ldexpf(1.f, c - one);
+        need += ZP ? (pc > hiO || pc < loO) : (fabsf(pc) > hiO);
+    }
 #pragma unroll
-            for (int j = 0; j < G; ++j)
-                if (j != i) acc += elem_err<ZP>(pj(j), s_ms[j], cc);
-            acc += elem_err<ZP>(pc, msc, cc);
+    for (int off = 32; off > 0; off >>= 1) need = max(need, __shfl_xor(need, off, kWave));
+
+    const Cfg base = ZP ? make_cfg<ZP>(hiO, loO) : make_cfg<ZP>(hiO, 0.f);
+    double e_base = 0.0;
+    // slot 0 = base configuration; slot u >= 1 = candidate n_cand - u.  Candidates below the
+    // slots stretch no lane's range, so the base configuration is theirs.
+    const int slots = min(need, n_cand) + 1;
+    for (int u = 0; u < slots; ++u) {
+#pragma unroll
+        for (int k = 0; k < CH / 2; ++k) asm volatile("" : "+v"(pk[k]));
+        const int c = n_cand - u;
+        float pc = 0.f;
+        double msc = 0.0;
+        const Cfg cf = u == 0 ? base : own_cfg(c, pc, msc);
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) acc = elem_acc<ZP>((double)pj(j), ms_p[j], cf, acc);
+        if (u == 0) {
+            e_base = acc;
+        } else {
+            const double e = wave_sum(elem_acc<ZP>((double)pc, msc, cf, acc));
+            if (lane == 0) sm_wave[wave][c] = e;
         }
-        acc = wave_sum(acc);
-        if (lane == 0) sm_wave[wave][c] = acc;
+    }
+    for (int c = 0; c < n_cand - (slots - 1); ++c) {
+        float pc;
+        double msc;
+        own(c, pc, msc);
+        const double e = wave_sum(elem_acc<ZP>((double)pc, msc, base, e_base));
+        if (lane == 0) sm_wave[wave][c] = e;
     }
     __syncthreads();
     if (tid < n_cand) {
@@ -256,7 +305,8 @@ GreedyPlan plan_greedy(int64_t K, int64_t N, int group_size, int n_cand) {
     GreedyPlan p{};
     p.group_size = group_size;
     p.groups = K / group_size;
-    p.n_slices = (N + kThreads - 1) / kThreads;
+    const int cols = kThreads / (group_size / 32);   // output columns per workgroup
+    p.n_slices = (N + cols - 1) / cols;
     p.n_cand = n_cand;
     p.part_stride = p.groups * p.n_slices * n_cand;
     size_t off = 0;
