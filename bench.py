@@ -18,12 +18,15 @@ Also reported on the same JSON line:
   multi_search  the joint search of the q, k and v projections of a 70B-shaped block, which read
                 one X [4096, 8192] (W [8192, 8192 | 1024 | 1024]), against the three searches
                 run one by one and against the bf16 matrix-core peak;
+  greedy        the power-of-two per-group greedy (20 candidates, 3 passes) on the same layer,
+                a VALU-bound workload: element evaluations per second against the vector-ALU
+                peak divided by the 7 operations one exact evaluation needs;
   gemv          the M = 1 W4A16 product over the seven linears of a 70B-shaped block
                 (462 MB of packed weights, rotated so the 256 MB Infinity Cache cannot hold
                 them) against HBM peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv] [--no-clip]
-                    [--no-multi]
+                    [--no-multi] [--no-greedy]
 """
 from __future__ import annotations
 
@@ -41,6 +44,8 @@ sys.path.insert(0, HERE)
 METRIC = "AWQ search TFLOP/s (% bf16 MFMA peak), 4096x4096 layer, 8192 calib tokens"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_VALU_TOPS = 39.32         # 256 CU x 4 SIMD x 16 lanes x 2.4 GHz: vector ops/s (fp32 unpacked = fp64 rate)
+GREEDY_OPS_PER_EVAL = 7        # multiply, round, clamp (2), fma, multiply, fma: one exact element error
 
 
 def log(msg):
@@ -57,6 +62,8 @@ def parse():
     ap.add_argument("--no-clip", action="store_true")
     ap.add_argument("--clip-iters", type=int, default=5)
     ap.add_argument("--no-multi", action="store_true")
+    ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--greedy-iters", type=int, default=3)
     ap.add_argument("--multi-iters", type=int, default=3)
     ap.add_argument("--gemv-iters", type=int, default=50)
     ap.add_argument("--cpu-cols", type=int, default=4096,
@@ -223,6 +230,9 @@ def main():
         out["clip_search"] = bench_clip(A, torch, dev, X, W, s_best, g, layer.zero_point, ws_search, stream,
                                         args.clip_iters)
 
+    if not args.no_greedy:
+        out["greedy"] = bench_greedy(A, torch, dev, W, mean_abs, g, stream, args.greedy_iters)
+
     if not args.no_multi:
         out["multi_search"] = bench_multi(A, I, torch, dev, args.multi_iters)
 
@@ -261,6 +271,38 @@ def bench_clip(A, torch, dev, X, W, s_best, g, zp, ws, stream, iters):
     return {"workload": "c2 layer at s*: 21 clip ratios 1 .. 0.5", "ms": round(ms, 4), "achieved": round(tf, 3),
             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "best_index": int(best.item()),
             "best_ratio": float(cbest.item())}
+
+
+def bench_greedy(A, torch, dev, W, mean_abs, g, stream, iters):
+    """The power-of-two greedy over the same layer's scales: 20 candidates, 3 passes, asymmetric."""
+    K, N = W.shape
+    cfg = A.qconfig(g, True, 21)
+    ws = A.workspace(A.awq_greedy_workspace_size(K, N, cfg, 20), dev)
+    s = torch.empty(K, dtype=torch.float32, device=dev)
+    er = torch.empty(K // g, dtype=torch.float64, device=dev)
+    e = torch.empty_like(er)
+    A.awq_greedy_search(W, mean_abs, cfg, 20, 3, ws, s, er, e, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        A.awq_greedy_search(W, mean_abs, cfg, 20, 3, ws, s, er, e, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    evals = 3.0 * K * 20 * N * g            # passes x K x candidates x N x g element evaluations
+    rate = evals / (ms * 1e-3) / 1e12
+    peak = PEAK_VALU_TOPS / GREEDY_OPS_PER_EVAL
+    ratio = float(er.sum().item() / e.sum().item())
+    log(f"[bench] greedy {ms:.2f} ms ({ms * 1e3 / (3 * g):.1f} us per step) -> {rate:.2f} T evals/s, "
+        f"rounding error / greedy error = {ratio:.3f}")
+    return {"workload": "c2 layer: power-of-two greedy, 20 candidates 2^-10..2^9, 3 passes, g=128 asymmetric",
+            "ms": round(ms, 3), "launches": 3 * g + 2,
+            "roofline": {"bound": "alu", "achieved": round(rate, 3), "peak": round(peak, 3),
+                         "unit": "T element-evaluations/s", "frac": round(rate / peak, 4), "traffic": None},
+            "algorithmic_evals_per_call": evals, "err_rtn_over_err": round(ratio, 4),
+            "scales_above_1": int((s > 1).sum().item()), "scales_below_1": int((s < 1).sum().item())}
 
 
 def bench_multi(A, I, torch, dev, iters):
