@@ -23,7 +23,10 @@ Also reported on the same JSON line:
                 peak divided by the 7 operations one exact evaluation needs;
   gemv          the M = 1 W4A16 product over the seven linears of a 70B-shaped block
                 (462 MB of packed weights, rotated so the 256 MB Infinity Cache cannot hold
-                them) against HBM peak.
+                them) against HBM peak;
+  gemv_fused    the same block with the projections that share an input searched jointly
+                (awq_search_multi), so q|k|v and gate|up share s and run as one product each
+                (4 launches instead of 7).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv] [--no-clip]
                     [--no-multi] [--no-greedy]
@@ -238,6 +241,7 @@ def main():
 
     if not args.no_gemv:
         out["gemv"] = bench_gemv(A, I, torch, dev, args.gemv_iters)
+        out["gemv_fused"] = bench_gemv_fused(A, I, torch, dev, args.gemv_iters)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_cols} columns")
@@ -355,6 +359,56 @@ def bench_multi(A, I, torch, dev, iters):
             "best_index": int(best.item())}
 
 
+def _gemv_bytes(K, N, g=128):
+    return K * N // 2 + 4 * (K // g) * N + (K // g) * N + 4 * K + 2 * K + 2 * N
+
+
+def bench_gemv_fused(A, I, torch, dev, iters):
+    """M = 1 block with q|k|v and gate|up each searched jointly and packed side by side."""
+    log("[bench] gemv_fused: joint searches of q,k,v and gate,up; o and down alone")
+    cfg = A.qconfig(128, True, 21)
+    groups = (("qkv", 0, (0, 1, 2)), ("o", 1, (3,)), ("gate_up", 2, (4, 5)), ("down", 3, (6,)))
+    layers = []
+    for name, j, ls in groups:
+        X = I.c5_input(0, j).to(dev)
+        Ws = [I.c5_weight(0, l).to(dev) for l in ls]
+        qs = A.run_multi(X, Ws, cfg)["q"]
+        del Ws
+        q = A.Quantized(torch.cat([u.codes for u in qs], 1).contiguous(), torch.cat([u.scales for u in qs], 1).contiguous(),
+                        torch.cat([u.zeros for u in qs], 1).contiguous(), qs[0].s, 128)
+        K, N = X.shape[1], q.codes.shape[1]
+        x1 = X[:1].contiguous()
+        del X, qs
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        ws = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
+        layers.append((name, K, N, x1, q, y, ws, _gemv_bytes(K, N)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def block():
+        for (name, K, N, x1, q, y, ws, byts) in layers:
+            A.awq_w4a16_gemm(x1, q.s, q.codes, q.scales, q.zeros, 128, y, ws, stream)
+
+    for _ in range(3):
+        block()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        block()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    total = sum(l[-1] for l in layers)
+    gbs = total / (ms * 1e-3) / 1e9
+    log(f"[bench] gemv_fused block {ms * 1e3:.2f} us -> {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM)")
+    return {"workload": "c5 block M=1 with shared-input projections fused: q|k|v [8192x10240], o [8192x8192], "
+                        "gate|up [8192x57344], down [28672x8192] (462 MB rotated per iteration)",
+            "iters": iters, "block_us": round(ms * 1e3, 2), "block_bytes": total, "achieved_GBs": round(gbs, 1),
+            "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def bench_gemv(A, I, torch, dev, iters):
     """M = 1 W4A16 product over the seven linears of the 70B-shaped block.  Each layer is run
     through stats -> search -> pack once (untimed) to produce its packed weights."""
@@ -371,7 +425,7 @@ def bench_gemv(A, I, torch, dev, iters):
         x1 = xs[j][:1].contiguous()
         y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
         ws = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
-        byts = K * N // 2 + 4 * (K // 128) * N + (K // 128) * N + 4 * K + 2 * K + 2 * N
+        byts = _gemv_bytes(K, N)
         layers.append((name, K, N, x1, q, y, ws, byts))
     xs.clear()
     torch.cuda.synchronize()

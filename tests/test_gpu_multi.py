@@ -8,7 +8,9 @@ step 4c over the projections.  Bars as for the single search: every joint and pe
 within 1e-2 relative of the oracle, the chosen alpha's oracle loss within 1e-2 of the oracle
 minimum, s_best equal to the GPU scale table's row; and, where every projection has a multiple of
 16 columns, the joint losses bit-identical to awq_search on the column-concatenated matrix (the
-same tiles in the same order).
+same tiles in the same order).  Packed side by side at the shared s, the projections are the
+packing of the concatenated matrix (bit-exact) and one W4A16 call serves them all (relative
+Frobenius error <= 2e-2 against the fp64 product, the single-layer bar).
 """
 import numpy as np
 import pytest
@@ -147,3 +149,31 @@ def test_multi_full_size_attention_projections():
     log(f"[multi] c5 qkv: X {tuple(X.shape)}, W {[tuple(W.shape) for W in Ws]}")
     L, E, b = _same_as_fused_and_single(A, X, Ws, A.qconfig(128, True, 21))
     log(f"[multi] c5 qkv: alpha* {int(b.item())}, L(alpha*) {float(L[b].item()):.6e}")
+
+
+def test_projections_sharing_s_run_as_one_product():
+    # packing is per column, so the jointly searched projections packed side by side are the
+    # packing of the concatenated matrix; one W4A16 call over it gives every projection's output
+    A = awq()
+    X, Ws = _inputs(300, 256, (48, 16, 64), 67)
+    r = A.run_multi(X.to(DEV), [W.to(DEV) for W in Ws], A.qconfig(128, True, 21))
+    qs = r["q"]
+    cat = A.Quantized(torch.cat([q.codes for q in qs], 1).contiguous(), torch.cat([q.scales for q in qs], 1).contiguous(),
+                      torch.cat([q.zeros for q in qs], 1).contiguous(), qs[0].s, 128)
+    Wc = torch.cat(Ws, 1).contiguous()
+    cw = torch.empty((256 // 8, 128), dtype=torch.int32, device=DEV)
+    cs = torch.empty((2, 128), dtype=torch.float32, device=DEV)
+    cz = torch.empty((2, 128), dtype=torch.uint8, device=DEV)
+    A.awq_pack(Wc.to(DEV), r["s_best"], A.qconfig(128, True, 21), cw, cs, cz)
+    torch.cuda.synchronize()
+    assert torch.equal(cw, cat.codes) and torch.equal(cs, cat.scales) and torch.equal(cz, cat.zeros)
+    for M in (1, 16):
+        xm = X[:M].to(DEV).contiguous()
+        Y = A.gemm(xm, cat)
+        torch.cuda.synchronize()
+        Yo = O.w4a16_ref(I.bf16_to_f64(X[:M]), r["s_best"].cpu().numpy(), cat.codes.cpu().numpy().view(np.uint32),
+                         cat.scales.cpu().numpy(), cat.zeros.cpu().numpy(), 128)
+        Yg = I.bf16_to_f64(Y.cpu())
+        rel = np.linalg.norm(Yg - Yo) / np.linalg.norm(Yo)
+        log(f"[multi] fused product M={M}: rel err {rel:.2e}")
+        assert rel <= 2e-2   # the W4A16 bar of the single-layer parity tests
