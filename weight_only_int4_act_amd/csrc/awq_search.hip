@@ -211,7 +211,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     constexpr int SPAD = 2;              // entries between scale and reciprocal rows (LDS banks)
     constexpr int NSTG = NWE + 2 * NSE + SPAD;   // staged 16-byte entries per group
     constexpr int NSTGP = 2 * NW * 64;   // staging entries incl. padding (two per thread)
-    static_assert(NW == 8 && NA < NW && NSTG <= NSTGP, "tile shape");
+    static_assert(NW == 8 && NA < NW && NA >= NW / 2 && NSTG <= NSTGP, "tile shape");   // waves 0-3 always own a slot
 
     const int tile = xcd_tile(blockIdx.x, tiles_per_xcd);
     if (tile >= n_tiles) return;
@@ -406,8 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             e[5] = fmaf(level(v[5] * rd), d, -v[5]) * rowbcast<13>(sv[c]);
             e[6] = fmaf(level(v[6] * rd), d, -v[6]) * rowbcast<14>(sv[c]);
             e[7] = fmaf(level(v[7] * rd), d, -v[7]) * rowbcast<15>(sv[c]);
-            if (wave < NA)   // the spare wavefront computes a duplicate and stores nothing
-                Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+            Es[ebuf][slot][c][lane] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                                                 pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
         }
     };
@@ -471,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     for (int g = 0; g < 4; ++g) stage(min(g, n_groups - 1), g);
     wait_vmcnt<0>();
     lds_barrier();
-    compute_E(0, 0, false);
+    if (wave < NA) compute_E(0, 0, false);   // the spare wavefront has no alpha slot
     lds_barrier();
 
     // Main loop.  The two wavefronts that share a SIMD (w and w + 4) run the two halves of a
