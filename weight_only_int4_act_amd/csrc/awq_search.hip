@@ -671,10 +671,10 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     p.n_grid = n_grid;
     p.zero_point = zero_point;
     // rows per workgroup: 640 (RBW = 5) unless its padding of T exceeds 512-row tiles' by more than
-    // the ~4.5% it gains per row (measured on the 4096x4096 layer); the clipped quantizer needs the
-    // registers of the 512-row tile.  The workspace holds either shape.
+    // the ~4.5% it gains per row (measured on the 4096x4096 layer).  The workspace holds either
+    // shape.
     const int64_t pad5 = (T + 639) / 640 * 640, pad4 = (T + 511) / 512 * 512;
-    p.variant = !clip && pad5 * 1000 <= pad4 * 1045 ? 5 : 4;   // row blocks per wavefront
+    p.variant = pad5 * 1000 <= pad4 * 1045 ? 5 : 4;   // row blocks per wavefront
     const int64_t xt_rows = pad5 > pad4 ? pad5 : pad4;
     const int64_t max_tb = (T + 511) / 512;
     p.na = kNA;
