@@ -10,34 +10,64 @@
 // With a clip ratio c (the configuration's optional min-max clipping, "009. AWQ Integration",
 // 关键设计 5) both ends of the range are multiplied by c before the step and the zero are formed.
 // The quantizer is evaluated in float64.  p = s*w is exact there (a float32 times a bf16 has at
-// most 32 significant bits), max/min are exact, and every division and rounding is a single
-// IEEE operation, so codes, steps and zeros are reproducible bit for bit by any float64
+// most 32 significant bits), max/min are exact, the step and the zero come from single IEEE
+// divisions, and each code is the round-half-even of p/Delta exactly as a float64 division and
+// rint give it (rne_div), so codes, steps and zeros are reproducible bit for bit by any float64
 // evaluation of the same definition.
-//
-// One thread per (group, output column): consecutive lanes read consecutive columns of a row,
-// so every load and store is coalesced across the wavefront.
 #include "awq_device.h"
 #include "awq_internal.h"
 
 namespace awq {
 
-template <bool ZP>
+// rne(p / d) for the quantizer's quotients, exactly as a float64 division followed by rint: with r
+// within two ulps of 1/d the product p*r rounds to the right integer unless p/d is exactly a
+// half-integer (p has at most 32 significant bits and d 24, so any other quotient is more than
+// 2^-34 from a half-integer, far beyond the product's error); the exact residual p - n d settles
+// that case, and round-half-to-even picks the even neighbour.
+__device__ __forceinline__ double rne_div(double p, double d, double r) {
+    double n = rint(p * r);
+    const double res = fma(-n, d, p);   // exact: n*d and p are within a factor 2 of each other
+    const double h = 0.5 * d;
+    if (fabs(res) >= h) {               // a half-integer quotient (or a last-bit slip of p*r)
+        const double m = res > 0.0 ? n + 1.0 : n - 1.0;   // the other neighbour
+        if (fabs(res) > h) n = m;
+        else if (((int64_t)n) & 1) n = m;
+    }
+    return n;
+}
+
+// One thread per (group, output column): the group's G weights of the column are loaded first
+// (consecutive lanes read consecutive columns of a row: every load is coalesced), then the range,
+// the step and zero, and the codes are formed from registers.
+template <int G, bool ZP>
 __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                              const float* __restrict__ s, int G, double clip,
+                                              const float* __restrict__ s, double clip,
                                               uint32_t* __restrict__ codes, float* __restrict__ scales,
                                               uint8_t* __restrict__ zeros) {
+    __shared__ float sg[G];   // the group's scales, shared by the workgroup's columns
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t jg = blockIdx.y;
-    if (n >= N) return;
     const int64_t k0 = jg * G;
+    for (int i = threadIdx.x; i < G; i += blockDim.x) sg[i] = s[k0 + i];
+    __syncthreads();
+    if (n >= N) return;
+    uint32_t wp[G / 2];   // bf16 pairs (rows 2i, 2i+1)
+#pragma unroll
+    for (int i = 0; i < G; i += 2)
+        wp[i / 2] = (uint32_t)W[(k0 + i) * N + n] | ((uint32_t)W[(k0 + i + 1) * N + n] << 16);
+    auto pv = [&](int i) {   // p = s*w, exact in float64
+        const uint32_t h = wp[i / 2];
+        return (double)sg[i] * (double)((i & 1) ? bf16_hi(h) : bf16_lo(h));
+    };
     double mx = 0.0, mn = 0.0, am = 0.0;
+#pragma unroll
     for (int i = 0; i < G; ++i) {
-        const double pv = (double)s[k0 + i] * (double)bf16_lo((uint32_t)W[(k0 + i) * N + n]);
+        const double p = pv(i);
         if (ZP) {
-            mx = fmax(mx, pv);
-            mn = fmin(mn, pv);
+            mx = fmax(mx, p);
+            mn = fmin(mn, p);
         } else {
-            am = fmax(am, fabs(pv));
+            am = fmax(am, fabs(p));
         }
     }
     // min-max clipping: both ends of the range scaled by the ratio (1: none), codes clamp below
@@ -56,13 +86,17 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
         z = 8.0;
     }
     const double dd = (double)d;
+    const double r = 1.0 / dd;
+    // recompute p in the second pass rather than keep G float64 values live from the first
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < G / 2; ++i) asm volatile("" : "+v"(wp[i]));
+#pragma unroll
     for (int i = 0; i < G; i += 8) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t k = k0 + i + j;
-            const double pv = (double)s[k] * (double)bf16_lo((uint32_t)W[k * N + n]);
-            double c = rint(pv / dd);
+            double c = rne_div(pv(i + j), dd, r);
             c = ZP ? fmin(fmax(c + z, 0.0), 15.0) : fmin(fmax(c, -7.0), 7.0) + 8.0;
             word |= (uint32_t)c << (4 * j);
         }
@@ -77,10 +111,16 @@ hipError_t launch_pack(const uint16_t* W, int64_t K, int64_t N, const float* s, 
                        hipStream_t st) {
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / group_size));
     const double clip = clip_ratio > 0.f && clip_ratio < 1.f ? (double)clip_ratio : 1.0;
-    if (zero_point)
-        k_pack<true><<<grid, 256, 0, st>>>(W, K, N, s, group_size, clip, codes, scales, zeros);
-    else
-        k_pack<false><<<grid, 256, 0, st>>>(W, K, N, s, group_size, clip, codes, scales, zeros);
+    if (group_size == 32) {
+        if (zero_point) k_pack<32, true><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+        else k_pack<32, false><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+    } else if (group_size == 64) {
+        if (zero_point) k_pack<64, true><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+        else k_pack<64, false><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+    } else {
+        if (zero_point) k_pack<128, true><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+        else k_pack<128, false><<<grid, 256, 0, st>>>(W, K, N, s, clip, codes, scales, zeros);
+    }
     return hipGetLastError();
 }
 
