@@ -72,22 +72,36 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(const uint16_t*
     }
 }
 
+// sum_abs[k] = sum over the chunks of partial[chunk][k] (+ the held value when accumulating);
+// mean_abs[k] = float32(sum / total_tokens).  A workgroup takes 32 channels; thread (c, l) adds
+// chunks l, l + 8, ... of channel c and the 8 sums of a channel are added in lane order through
+// LDS, so many loads are in flight even for a few thousand channels.  The partial sums of |bf16|
+// values are exact in float64, so the order does not change the result.
 __global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ partial, int64_t chunks, int64_t K,
                                                      double* __restrict__ sum_abs, int accumulate,
                                                      int64_t total_tokens, float* __restrict__ mean_abs) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
-    double s = 0.0;
-    for (int64_t c0 = 0; c0 < chunks; c0 += 8) {   // 8 loads in flight, added in the same fixed order
+    __shared__ double sm[8][32];
+    const int c = threadIdx.x & 31, l = threadIdx.x >> 5;
+    const int64_t k = (int64_t)blockIdx.x * 32 + c;
+    const int64_t kk = k < K ? k : K - 1;
+    double t = 0.0;
+    for (int64_t b0 = l; b0 < chunks; b0 += 8 * 8) {   // 8 loads in flight per thread
         double v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = c0 + j < chunks ? partial[(c0 + j) * K + k] : 0.0;
+        for (int j = 0; j < 8; ++j) v[j] = b0 + 8 * j < chunks ? partial[(b0 + 8 * j) * K + kk] : 0.0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s += v[j];
+        for (int j = 0; j < 8; ++j) t += v[j];
     }
-    if (accumulate) s = sum_abs[k] + s;
-    sum_abs[k] = s;
-    if (mean_abs) mean_abs[k] = (float)(s / (double)total_tokens);
+    sm[l][c] = t;
+    __syncthreads();
+    if (l == 0 && k < K) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += sm[i][c];
+        if (accumulate) s = sum_abs[k] + s;
+        sum_abs[k] = s;
+        if (mean_abs) mean_abs[k] = (float)(s / (double)total_tokens);
+    }
 }
 
 StatsPlan plan_stats(int64_t T, int64_t K) {
@@ -115,8 +129,8 @@ hipError_t launch_stats(const uint16_t* X, int64_t T, int64_t K, double* sum_abs
         k_stats_partial<false><<<grid, kStatsThreads, 0, st>>>(X, T, K, p.rows_per_chunk, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_stats_final<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(partials, p.chunks, K, sum_abs, accumulate,
-                                                              total_tokens, mean_abs);
+    k_stats_final<<<(unsigned)((K + 31) / 32), 256, 0, st>>>(partials, p.chunks, K, sum_abs, accumulate,
+                                                            total_tokens, mean_abs);
     return hipGetLastError();
 }
 
