@@ -8,11 +8,11 @@
 //
 // The walk is sequential inside a group (each decision sees the previous ones) but the error of
 // one decision is a sum over all N output columns, and the K/g groups are independent.  One launch
-// handles one decision step for every group at once: a thread owns one output column of one group
-// and scores every candidate for the step's channel; per-candidate sums leave each workgroup as
-// float64 partials.  The next launch's workgroups read those partials in a fixed order and take
-// the decision redundantly (every workgroup of a group reaches the same one), so no workgroup ever
-// waits on another.
+// handles one decision step for every group at once: the g channels of an output column are split
+// over g/32 lanes of one wavefront, which score every candidate for the step's channel; the
+// per-candidate sums leave each workgroup as float64 partials.  The next launch's workgroups read
+// those partials in a fixed order and take the decision redundantly (every workgroup of a group
+// reaches the same one), so no workgroup ever waits on another.
 //
 // Exactness.  With power-of-two scales p = s*w is a bf16 value (8 significant bits) and Delta a
 // float32 (24), so p/Delta is either exactly a half-integer or more than 2^-25 away from one.
@@ -20,19 +20,19 @@
 // its nearest integer is the packing quantizer's code except at exact half-integers, where either
 // neighbour gives the same squared error (the two errors are +-Delta/2, and at the ends of the
 // range both clamp to the same level).  The zero point, which does change the codes, settles its
-// exact half-integers with an exact residual.  The weighted error of an element, m (What - w) = (m/s) (level*Delta
-// - p), is exact: level*Delta - p is a multiple of Delta's last bit no larger than Delta/2, and
-// its product with m/s needs at most 48 bits.  Only the float64 sums of squares round, so every
-// decision matches a float64 evaluation of the definition except between candidates whose errors
-// differ by about 1e-16 relative.
+// exact half-integers with an exact residual.  The weighted error of an element,
+// m (What - w) = (m/s) (level*Delta - p), is exact: level*Delta - p is a multiple of Delta's last
+// bit no larger than Delta/2, and its product with m/s needs at most 48 bits.  Only the float64
+// sums of squares round, so every decision matches a float64 evaluation of the definition except
+// between candidates whose errors differ by about 1e-16 relative.
 //
 // Work.  A candidate that keeps the channel's scaled weight inside the range of the other
 // channels leaves the group's step and zero unchanged: its error is the others' error at the base
 // configuration plus its own element.  Only candidates that stretch the range need the whole
 // group again, and those are the largest ones (|c w| grows with c).  Each wavefront therefore
 // evaluates the others' error for the base configuration and for the top S candidates, S the most
-// any of its lanes needs, one configuration per pass over the column; the rest cost one element
-// each.
+// any of its columns needs, one configuration per pass over the channels; the rest cost one
+// element each.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -95,7 +95,7 @@ __device__ __forceinline__ double elem_acc(double p, double ms, const Cfg& c, do
 
 // The decision of one step for one group, taken from the previous launch's partials:
 // part[(slice * n_cand + c)] for slice < n_slices.  Every workgroup of the group computes the
-// same sums in the same order.  Returns the chosen candidate index; *cur is the channel's index
+// same sums in the same order.  Returns the chosen candidate index; cur is the channel's index
 // before the step (a value already updated by a concurrent writer gives the same answer, since
 // the rule keeps a candidate that is already a minimum).
 __device__ int decide(const double* __restrict__ part, int n_slices, int n_cand, int cur, double* sm_chunk,
