@@ -8,7 +8,10 @@
  *   2. the per-layer scale search over alpha_i = i/(n_grid-1), scoring
  *      L(alpha) = || X (S^-1 Q(S W) - W) ||^2 with S = diag(m^alpha);
  *   3. INT4 packing of the winning S* W (codes, per-group scales and zeros) and
- *      the W4A16 product Y = (X / s*) Dequant(Wq).
+ *      the W4A16 product Y = (X / s*) Dequant(Wq);
+ *   4. variants of the search: over a caller's scale table (other statistics and
+ *      scale families), over clip ratios, jointly over projections that share X, and
+ *      the power-of-two per-group greedy of [P4].
  *
  * Sources (page title -- section), for the definitions cited below:
  *   [P1] "AWQ (Activation-aware Weight Quantization)" (compassingai.com)
@@ -68,8 +71,8 @@ extern "C" {
  *               range (0 included; max|p| in symmetric mode) are multiplied by c before Delta
  *               and the zero are formed, and codes beyond the clipped range clamp to its end
  *               levels.  0 or 1 = no clipping (so a zero-initialised struct needs no value);
- *               values in (0, 1) clip.  awq_search and awq_pack use it; awq_clip_search
- *               ignores it.
+ *               values in (0, 1) clip.  awq_search, awq_search_table, awq_search_multi and
+ *               awq_pack use it; awq_clip_search ignores it; awq_greedy_search rejects it.
  */
 typedef struct awq_qconfig {
     int32_t w_bit;
