@@ -194,21 +194,26 @@ constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
 constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 constexpr int kGemvGpw = 1;      // groups per wavefront
 
-template <int G>
+// VG: rows a wavefront takes at a time, a divisor of the quantization group G.  Narrow layers
+// split each group into G/VG slices (each with the group's step and zero, and the sum of x' over
+// its own rows in the offset/zero correction, which is linear in the rows), so that more
+// workgroups share K and fill the GPU.
+template <int G, int VG>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
                                                     const uint32_t* __restrict__ codes,
                                                     const float* __restrict__ scales,
                                                     const uint8_t* __restrict__ zeros, int K, int N,
                                                     uint16_t* __restrict__ Y, float* __restrict__ part) {
-    constexpr int R = G / 8;                     // code rows per group
-    constexpr int NG = kGemvWaves * kGemvGpw;    // groups per workgroup
-    // x' of the workgroup's groups: group slot i, code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
-    __shared__ uint32_t xpair[NG][G / 2];
+    static_assert(G % VG == 0 && VG >= 32, "slice of a group");
+    constexpr int R = VG / 8;                    // code rows per slice
+    constexpr int NG = kGemvWaves * kGemvGpw;    // slices per workgroup
+    // x' of the workgroup's slices: slot i, code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
+    __shared__ uint32_t xpair[NG][VG / 2];
     __shared__ float sxs[NG];
     __shared__ float red[kGemvWaves][kGemvCols];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
-    const int n_groups = K / G;
+    const int n_groups = K / VG;                 // slices, from here on called groups
     const int n0 = cb * kGemvCols + lane * 4;
     const bool nvalid = n0 < N;                  // N % 4 == 0
     const int nc = nvalid ? n0 : N - 4;
@@ -225,21 +230,22 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
         const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
 #pragma unroll
         for (int r = 0; r < R; ++r) b.cw[r] = *(const u32x4*)(cbase + (int64_t)r * N);
-        b.dsc = *(const floatx4*)(scales + (int64_t)gg * N + nc);
-        b.zw = *(const uint32_t*)(zeros + (int64_t)gg * N + nc);
+        const int qg = gg / (G / VG);            // the quantization group of the slice
+        b.dsc = *(const floatx4*)(scales + (int64_t)qg * N + nc);
+        b.zw = *(const uint32_t*)(zeros + (int64_t)qg * N + nc);
     };
-    // x' of the workgroup's NG groups in pair order: thread t forms pair t % (G/2) of group slot
-    // t / (G/2); the group sums come from a fixed butterfly over the G/2 lanes of a group.  The
+    // x' of the workgroup's NG slices in pair order: thread t forms pair t % (VG/2) of slot
+    // t / (VG/2); the slice sums come from a fixed butterfly over the VG/2 lanes of a slice.  The
     // activation and scale loads are issued before the code loads (loads complete in order), so
     // x' is formed while the codes are still in flight.
-    constexpr int XI = (NG * (G / 2) + 255) / 256;   // pairs per thread
+    constexpr int XI = (NG * (VG / 2) + 255) / 256;  // pairs per thread
     float xa[XI][2], sa[XI][2];
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const int t = 256 * u + (int)threadIdx.x;
-        const int slot = t / (G / 2), l = t % (G / 2);
+        const int slot = t / (VG / 2), l = t % (VG / 2);
         const int gg = min(kb * NG + min(slot, NG - 1), n_groups - 1);
-        const int k1 = gg * G + 8 * (l >> 2) + (l & 3), k2 = k1 + 4;
+        const int k1 = gg * VG + 8 * (l >> 2) + (l & 3), k2 = k1 + 4;
         xa[u][0] = bf16_lo((uint32_t)X[k1]);
         xa[u][1] = bf16_lo((uint32_t)X[k2]);
         sa[u][0] = s[k1];
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const int t = 256 * u + (int)threadIdx.x;
-        const int slot = t / (G / 2), l = t % (G / 2);
+        const int slot = t / (VG / 2), l = t % (VG / 2);
         float sx = 0.f;
         if (slot < NG) {
             const __bf16 x1 = (__bf16)(xa[u][0] / sa[u][0]);
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                              ((uint32_t)__builtin_bit_cast(unsigned short, x2) << 16);
         }
 #pragma unroll
-        for (int o = 1; o < G / 2 && o < 64; o <<= 1) sx += __shfl_xor(sx, o, 64);
+        for (int o = 1; o < VG / 2 && o < 64; o <<= 1) sx += __shfl_xor(sx, o, 64);
         if (slot < NG && l == 0) sxs[slot] = sx;
     }
     __syncthreads();
@@ -385,7 +391,12 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     if (M == 1) {
         p.variant = 0;
         p.grid_x = (N + kGemvCols - 1) / kGemvCols;
-        p.grid_y = (n_groups + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
+        // narrow layers: halve the rows a wavefront takes (down to 32) until ~256 workgroups share
+        // the work
+        p.vgroup = group_size;
+        while (p.vgroup > 32 && p.grid_x * (K / p.vgroup) / (kGemvWaves * kGemvGpw) < 256) p.vgroup /= 2;
+        const int64_t n_slices = K / p.vgroup;
+        p.grid_y = (n_slices + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
         p.mpad = 1;
@@ -419,12 +430,19 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint3
     if (p.variant == 0) {
         float* part = (float*)((char*)ws + p.off_part);
         dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
+        const int vg = p.vgroup;
         if (group_size == 32)
-            k_w4a16_gemv<32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            k_w4a16_gemv<32, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        else if (group_size == 64 && vg == 64)
+            k_w4a16_gemv<64, 64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
         else if (group_size == 64)
-            k_w4a16_gemv<64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            k_w4a16_gemv<64, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        else if (vg == 128)
+            k_w4a16_gemv<128, 128><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+        else if (vg == 64)
+            k_w4a16_gemv<128, 64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
         else
-            k_w4a16_gemv<128><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            k_w4a16_gemv<128, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.grid_y == 1) return e;
         k_gemv_reduce<<<(unsigned)((N + 31) / 32), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);

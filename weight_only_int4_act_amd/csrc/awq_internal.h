@@ -90,6 +90,7 @@ struct GemmPlan {
     int64_t grid_x, grid_y, grid_z;
     int ksplit;              // workgroups along K (float32 partials added by a second kernel)
     int64_t mpad;            // M rounded up to the workgroup's row tile
+    int vgroup;              // M = 1: rows of a group a wavefront takes at a time
     // workspace layout (byte offsets): split-K partials, x' in fragment order, group sums of x'
     size_t off_part, off_xp, off_sg, ws_bytes;
 };
