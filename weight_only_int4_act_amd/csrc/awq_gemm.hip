@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
         const int gg = min(group_of(i), n_groups - 1);
         const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
 #pragma unroll
-        for (int r = 0; r < R; ++r) b.cw[r] = *(const u32x4*)(cbase + (int64_t)r * N);
+        for (int r = 0; r < R; ++r)   // read once: streaming (non-temporal) loads
+            b.cw[r] = __builtin_nontemporal_load((const u32x4*)(cbase + (int64_t)r * N));
         const int qg = gg / (G / VG);            // the quantization group of the slice
         b.dsc = *(const floatx4*)(scales + (int64_t)qg * N + nc);
         b.zw = *(const uint32_t*)(zeros + (int64_t)qg * N + nc);
@@ -391,10 +392,10 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     if (M == 1) {
         p.variant = 0;
         p.grid_x = (N + kGemvCols - 1) / kGemvCols;
-        // narrow layers: halve the rows a wavefront takes (down to 32) until ~256 workgroups share
-        // the work
+        // halve the rows a wavefront takes (down to 32) until there are ~1536 workgroups: about
+        // six per CU, enough that the last ones to finish leave little of the GPU idle
         p.vgroup = group_size;
-        while (p.vgroup > 32 && p.grid_x * (K / p.vgroup) / (kGemvWaves * kGemvGpw) < 256) p.vgroup /= 2;
+        while (p.vgroup > 32 && p.grid_x * (K / p.vgroup) / (kGemvWaves * kGemvGpw) < 1536) p.vgroup /= 2;
         const int64_t n_slices = K / p.vgroup;
         p.grid_y = (n_slices + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
         p.grid_z = 1;
