@@ -9,6 +9,9 @@
   full token count.
 * A 70B-block layer (8192 -> 1024, 4096 tokens) through search and pack, and the M=1 GEMV of
   the 8192 -> 28672 gate projection checked on sampled columns.
+* Every calibration token and the full K of the other configurations (8192 x 11008, 16384 x 5120
+  and the 70B block's 4096 x 28672 down projection) on the first 64 output columns: the token
+  tiling and the walk over K are those of the full layer; only the column tiles are fewer.
 """
 import numpy as np
 import pytest
@@ -88,3 +91,14 @@ def test_70b_block_kv_layer_and_gate_gemv():
     assert np.array_equal(gpu["scales"][:, cols], d) and np.array_equal(gpu["zeros"][:, cols], z)
     bad = O.unpack_nibbles(w) != O.unpack_nibbles(gpu["codes"][:, cols])
     assert bad.sum() == 0
+
+
+@pytest.mark.parametrize("cfg", ["c3", "c4", "c5.down"])
+def test_full_tokens_and_k_on_a_column_slice(cfg):
+    if cfg == "c5.down":
+        X, W, g, zp = I.c5_input(0, 3), I.c5_weight(0, 6), 128, True
+    else:
+        L0 = I.make_config(cfg, seed=0).layers[0]
+        X, W, g, zp = L0.X, L0.W, L0.group_size, L0.zero_point
+    L = I.Layer(f"{cfg}[:, :64]", X, W[:, :64].contiguous(), g, zp)
+    _check_layer(L, f"{cfg}[:, :64]", g, zp)
