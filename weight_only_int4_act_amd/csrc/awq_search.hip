@@ -500,12 +500,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int sbn = (jg + 1) & 3;           // group jg + 1
         const int sbn2 = (jg + 2) & 3;          // group jg + 2
         const int sjg = min(jg + 4, n_groups - 1);
+        const bool next = jg + 1 < n_groups;   // the last step has no E tile to prepare
         if (mfma_first) {
             mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn);
-            compute_E(sbn, buf ^ 1, true);
+            if (next) compute_E(sbn, buf ^ 1, true);
         } else {
             // the spare wavefront (no alpha slot of its own) skips the E half
-            if (wave < NA) compute_E(sbn, buf ^ 1, true);
+            if (wave < NA && next) compute_E(sbn, buf ^ 1, true);
             mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn2);
         }
         wait_vmcnt<2 * C * RBW - XS + 2>();
