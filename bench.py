@@ -26,10 +26,15 @@ Also reported on the same JSON line:
                 them) against HBM peak;
   gemv_fused    the same block with the projections that share an input searched jointly
                 (awq_search_multi), so q|k|v and gate|up share s and run as one product each
-                (4 launches instead of 7).
+                (4 launches instead of 7);
+  block_quantization  the quantization of that whole block at full size on the way there
+                (statistic, joint or single search and packing of each input group, one timed
+                pass each) against the bf16 matrix-core peak;
+  other_configs the statistic and search at full size on the 11008 -> 4096 layer (8192 tokens)
+                and the symmetric g = 64 5120 -> 13824 layer (16384 tokens).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemv] [--no-clip]
-                    [--no-multi] [--no-greedy]
+                    [--no-multi] [--no-greedy] [--no-configs]
 """
 from __future__ import annotations
 
@@ -66,6 +71,7 @@ def parse():
     ap.add_argument("--clip-iters", type=int, default=5)
     ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--greedy-iters", type=int, default=3)
     ap.add_argument("--multi-iters", type=int, default=3)
     ap.add_argument("--gemv-iters", type=int, default=50)
@@ -239,9 +245,12 @@ def main():
     if not args.no_multi:
         out["multi_search"] = bench_multi(A, I, torch, dev, args.multi_iters)
 
+    if not args.no_configs:
+        out["other_configs"] = bench_configs(A, I, torch, dev, 3)
+
     if not args.no_gemv:
         out["gemv"] = bench_gemv(A, I, torch, dev, args.gemv_iters)
-        out["gemv_fused"] = bench_gemv_fused(A, I, torch, dev, args.gemv_iters)
+        out["gemv_fused"], out["block_quantization"] = bench_gemv_fused(A, I, torch, dev, args.gemv_iters)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_cols} columns")
@@ -309,6 +318,53 @@ def bench_greedy(A, torch, dev, W, mean_abs, g, stream, iters):
             "scales_above_1": int((s > 1).sum().item()), "scales_below_1": int((s < 1).sum().item())}
 
 
+def bench_configs(A, I, torch, dev, iters):
+    """The search (statistic + 21-point search + argmin) at the full size of the other single-layer
+    configurations: the 11008 -> 4096 down projection with silu-like activations and 8192 tokens,
+    and the 5120 -> 13824 symmetric g=64 projection with 16384 tokens."""
+    res = {}
+    for name in ("c3", "c4"):
+        log(f"[bench] {name}: generating the full-size layer")
+        L = I.make_config(name, seed=0).layers[0]
+        X, W = L.X.to(dev), L.W.to(dev)
+        T, K = X.shape
+        N = W.shape[1]
+        cfg = A.qconfig(L.group_size, L.zero_point, 21)
+        stream = torch.cuda.current_stream()
+        sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+        m = torch.empty(K, dtype=torch.float32, device=dev)
+        ws_stats = A.workspace(A.awq_act_stats_workspace_size(T, K), dev)
+        ws = A.workspace(A.awq_search_workspace_size(T, K, N, cfg), dev)
+        losses = torch.empty(21, dtype=torch.float64, device=dev)
+        best = torch.empty(1, dtype=torch.int32, device=dev)
+        s_best = torch.empty(K, dtype=torch.float32, device=dev)
+
+        def search():
+            A.awq_act_stats(X, sum_abs, False, T, m, ws_stats, stream)
+            A.awq_search(X, W, m, cfg, ws, losses, best, s_best, stream)
+
+        search()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            search()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        flops = 21 * 2.0 * T * K * N
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"[bench] {name} ({T}x{K} -> {N}, g={L.group_size}, {'asym' if L.zero_point else 'sym'}): statistic + "
+            f"search {ms:.3f} ms -> {tf:.1f} TFLOP/s, alpha* {int(best.item())}")
+        res[name] = {"workload": f"{name}: T={T}, K={K}, N={N}, g={L.group_size}, "
+                                 f"{'asymmetric' if L.zero_point else 'symmetric'}, 21-point alpha grid",
+                     "ms": round(ms, 4), "algorithmic_flops": flops, "achieved": round(tf, 3), "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "best_index": int(best.item())}
+        del X, W, ws, L
+    return res
+
+
 def bench_multi(A, I, torch, dev, iters):
     """Joint search of q, k and v (one X) against the three single searches, same inputs."""
     log("[bench] multi: building X_attn [4096, 8192] and q, k, v")
@@ -364,24 +420,67 @@ def _gemv_bytes(K, N, g=128):
 
 
 def bench_gemv_fused(A, I, torch, dev, iters):
-    """M = 1 block with q|k|v and gate|up each searched jointly and packed side by side."""
-    log("[bench] gemv_fused: joint searches of q,k,v and gate,up; o and down alone")
+    """M = 1 block with q|k|v and gate|up each searched jointly and packed side by side.  The
+    quantization of each group (statistic, joint search, packing) is timed on the way: the whole
+    70B-shaped block at full size."""
+    log("[bench] gemv_fused: joint searches of q,k,v and gate,up; o and down alone (timed)")
     cfg = A.qconfig(128, True, 21)
+    stream = torch.cuda.current_stream()
     groups = (("qkv", 0, (0, 1, 2)), ("o", 1, (3,)), ("gate_up", 2, (4, 5)), ("down", 3, (6,)))
     layers = []
+    quant = {}
     for name, j, ls in groups:
         X = I.c5_input(0, j).to(dev)
         Ws = [I.c5_weight(0, l).to(dev) for l in ls]
-        qs = A.run_multi(X, Ws, cfg)["q"]
-        del Ws
-        q = A.Quantized(torch.cat([u.codes for u in qs], 1).contiguous(), torch.cat([u.scales for u in qs], 1).contiguous(),
-                        torch.cat([u.zeros for u in qs], 1).contiguous(), qs[0].s, 128)
-        K, N = X.shape[1], q.codes.shape[1]
+        T, K = X.shape
+        Ns = [W.shape[1] for W in Ws]
+        sum_abs = torch.empty(K, dtype=torch.float64, device=dev)
+        m = torch.empty(K, dtype=torch.float32, device=dev)
+        ws_stats = A.workspace(A.awq_act_stats_workspace_size(T, K), dev)
+        ws = A.workspace(A.awq_search_multi_workspace_size(T, K, Ns, cfg), dev)
+        losses = torch.empty(21, dtype=torch.float64, device=dev)
+        each = torch.empty((len(Ws), 21), dtype=torch.float64, device=dev)
+        best = torch.empty(1, dtype=torch.int32, device=dev)
+        s_best = torch.empty(K, dtype=torch.float32, device=dev)
+        outs = [(torch.empty((K // 8, n), dtype=torch.int32, device=dev),
+                 torch.empty((K // 128, n), dtype=torch.float32, device=dev),
+                 torch.empty((K // 128, n), dtype=torch.uint8, device=dev)) for n in Ns]
+
+        def quantize():
+            A.awq_act_stats(X, sum_abs, False, T, m, ws_stats, stream)
+            A.awq_search_multi(X, Ws, m, cfg, ws, losses, each, best, s_best, stream)
+            for W, (c, sc, z) in zip(Ws, outs):
+                A.awq_pack(W, s_best, cfg, c, sc, z, stream)
+
+        quantize()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        quantize()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        quant[name] = {"ms": e0.elapsed_time(e1), "flops": 21 * 2.0 * T * K * sum(Ns),
+                       "best_index": int(best.item())}
+        q = A.Quantized(torch.cat([o[0] for o in outs], 1).contiguous(), torch.cat([o[1] for o in outs], 1).contiguous(),
+                        torch.cat([o[2] for o in outs], 1).contiguous(), s_best, 128)
+        N = q.codes.shape[1]
         x1 = X[:1].contiguous()
-        del X, qs
+        del X, Ws, ws, outs
         y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-        ws = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
-        layers.append((name, K, N, x1, q, y, ws, _gemv_bytes(K, N)))
+        wsg = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
+        layers.append((name, K, N, x1, q, y, wsg, _gemv_bytes(K, N)))
+    qms = sum(v["ms"] for v in quant.values())
+    qfl = sum(v["flops"] for v in quant.values())
+    qtf = qfl / (qms * 1e-3) / 1e12
+    log(f"[bench] 70B block quantization (stats + joint searches + pack): {qms:.2f} ms, search flops "
+        f"{qfl / 1e12:.1f} TFLOP -> {qtf:.1f} TFLOP/s")
+    block_quant = {"workload": "c5 block, all 7 linears at full size, 4096 tokens: q,k,v searched jointly on X_attn, "
+                               "o alone, gate,up jointly on X_mlp, down alone (K=28672); each group = statistic + "
+                               "search + pack",
+                   "ms": round(qms, 3), "algorithmic_flops": qfl, "achieved": round(qtf, 3), "unit": "TFLOP/s",
+                   "frac": round(qtf / PEAK_BF16_TFLOPS, 4),
+                   "groups": {k: {"ms": round(v["ms"], 3), "best_index": v["best_index"]} for k, v in quant.items()}}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -406,7 +505,7 @@ def bench_gemv_fused(A, I, torch, dev, iters):
     return {"workload": "c5 block M=1 with shared-input projections fused: q|k|v [8192x10240], o [8192x8192], "
                         "gate|up [8192x57344], down [28672x8192] (462 MB rotated per iteration)",
             "iters": iters, "block_us": round(ms * 1e3, 2), "block_bytes": total, "achieved_GBs": round(gbs, 1),
-            "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}, block_quant
 
 
 def bench_gemv(A, I, torch, dev, iters):
