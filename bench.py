@@ -513,6 +513,7 @@ def bench_gemv(A, I, torch, dev, iters):
     through stats -> search -> pack once (untimed) to produce its packed weights."""
     layers = []
     xs = {}
+    xm = {}
     log("[bench] gemv: building the 70B-shaped block (7 linears, T=4096)")
     for l, (name, K, N, j) in enumerate(I.C5_LAYERS):
         if j not in xs:
@@ -522,6 +523,7 @@ def bench_gemv(A, I, torch, dev, iters):
         del Wl
         q = r["q"]
         x1 = xs[j][:1].contiguous()
+        xm[name] = {M: xs[j][:M].contiguous() for M in (16, 256)}
         y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
         ws = A.workspace(A.awq_w4a16_gemm_workspace_size(1, K, N, 128), dev)
         byts = _gemv_bytes(K, N)
@@ -567,6 +569,32 @@ def bench_gemv(A, I, torch, dev, iters):
         us = float(np.median([evs[it][li][0].elapsed_time(evs[it][li][1]) for it in range(iters)])) * 1e3
         res["layers"][name] = {"us": round(us, 2), "GBs": round(byts / (us * 1e-6) / 1e9, 1)}
     log(f"[bench] gemv block {res['block_us']} us -> {res['achieved_GBs']} GB/s ({100 * res['frac']:.1f}% of HBM)")
+    # the same block at M = 16 (weight bytes still dominate) and M = 256 (matrix cores)
+    res["M16_M256"] = {}
+    for M in (16, 256):
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for (name, K, N, *_r) in layers]
+        wss = [A.workspace(A.awq_w4a16_gemm_workspace_size(M, K, N, 128), dev) for (name, K, N, *_r) in layers]
+
+        def blockm():
+            for (name, K, N, x1, q, y, ws, byts), yy, ww in zip(layers, ys, wss):
+                A.awq_w4a16_gemm(xm[name][M], q.s, q.codes, q.scales, q.zeros, 128, yy, ww, stream)
+
+        blockm()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            blockm()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        flops = sum(2.0 * M * K * N for (name, K, N, *_r) in layers)
+        byts = total_bytes + sum(2 * M * (K + N) for (name, K, N, *_r) in layers)
+        res["M16_M256"][f"M{M}"] = {"block_us": round(ms * 1e3, 2), "GBs": round(byts / (ms * 1e-3) / 1e9, 1),
+                                    "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                                    "frac_bf16": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] block at M={M}: {ms * 1e3:.1f} us -> {byts / (ms * 1e-3) / 1e9:.0f} GB/s, "
+            f"{flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
     return res
 
 

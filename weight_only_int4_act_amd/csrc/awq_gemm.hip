@@ -108,35 +108,58 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t g = gb + wave; g < ge; g += 4) {
-        const floatx4 dsc = *(const floatx4*)(scales + g * N + nc);
-        const uint32_t zw = *(const uint32_t*)(zeros + g * N + nc);
+    // For MB <= 2 the code words, steps, zeros and x' sums of this wavefront's next group (and, for
+    // MB = 1, its x' fragments) are loaded before the current group's products are issued (two
+    // register buffers), so a group's memory reads are in flight during the previous group's
+    // matrix work; with 4 row blocks the accumulators leave no room for a second buffer.
+    constexpr bool XB = MB == 1;
+    struct Buf {
+        u32x4 cw[C];
+        floatx4 dsc;
+        uint32_t zw;
+        floatx4 sv[MB];
+        u32x4 a[XB ? C : 1][MB];
+    };
+    auto issue = [&](int64_t g, Buf& b) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) b.cw[c] = *(const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc);
+        b.dsc = *(const floatx4*)(scales + g * N + nc);
+        b.zw = *(const uint32_t*)(zeros + g * N + nc);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) b.sv[mb] = *(const floatx4*)(Sg + g * mpad + (R0 + mb) * 16 + 4 * q);
+        if constexpr (XB) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) b.a[c][mb] = Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
+        }
+    };
+    auto consume = [&](int64_t g, const Buf& b) {
         floatx4 accg[MB][4];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const floatx4 sv = *(const floatx4*)(Sg + g * mpad + (R0 + mb) * 16 + 4 * q);
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float off = -(128.f + (float)((zw >> (8 * j)) & 0xFFu));
+                const float off = -(128.f + (float)((b.zw >> (8 * j)) & 0xFFu));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accg[mb][j][i] = off * sv[i];
+                for (int i = 0; i < 4; ++i) accg[mb][j][i] = off * b.sv[mb][i];
             }
-        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const u32x4 cw = *(const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc);
             u32x4 a[MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) a[mb] = Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
+            for (int mb = 0; mb < MB; ++mb)
+                a[mb] = XB ? b.a[XB ? c : 0][mb] : Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
+            const u32x4 cw = b.cw[c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 // plain C (the compiler emits v_and_or_b32): these values feed the matrix core
                 // directly, and only code the compiler sees gets its VALU -> MFMA wait states
-                const u32x4 b = u32x4{(cw[j] & nib) | bf128, ((cw[j] >> 4) & nib) | bf128,
-                                      ((cw[j] >> 8) & nib) | bf128, ((cw[j] >> 12) & nib) | bf128};
+                const u32x4 bo = u32x4{(cw[j] & nib) | bf128, ((cw[j] >> 4) & nib) | bf128,
+                                       ((cw[j] >> 8) & nib) | bf128, ((cw[j] >> 12) & nib) | bf128};
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b),
+                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, bo),
                                                accg[mb][j]);
             }
         }
@@ -145,7 +168,26 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(dsc[j], accg[mb][j][i], acc[mb][j][i]);
+                for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(b.dsc[j], accg[mb][j][i], acc[mb][j][i]);
+    };
+    if constexpr (MB <= 2) {
+        // two groups per step, so each buffer keeps a fixed set of registers
+        Buf b0, b1;
+        if (gb + wave < ge) issue(gb + wave, b0);
+        for (int64_t g = gb + wave; g < ge; g += 8) {
+            if (g + 4 < ge) issue(g + 4, b1);
+            consume(g, b0);
+            if (g + 4 < ge) {
+                if (g + 8 < ge) issue(g + 8, b0);
+                consume(g + 4, b1);
+            }
+        }
+    } else {
+        for (int64_t g = gb + wave; g < ge; g += 4) {
+            Buf b;
+            issue(g, b);
+            consume(g, b);
+        }
     }
 
     if (wave > 0) {
@@ -357,6 +399,22 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
     }
 }
 
+// Y = bf16(sum_b part[b]) for the matrix-core path, where there are few partials (ksplit <= 8)
+// and many outputs: each thread adds the partials of 4 adjacent outputs in a fixed order (all its
+// loads issued before the sum) and writes 4 bf16 values.
+__global__ __launch_bounds__(256) void k_part_reduce4(const floatx4* __restrict__ part, int nkb, int64_t n4,
+                                                      uint2* __restrict__ Y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    floatx4 v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) v[b] = b < nkb ? part[b * n4 + i] : floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 t = v[0];
+#pragma unroll
+    for (int b = 1; b < 8; ++b) t += v[b];
+    Y[i] = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+}
+
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -381,7 +439,12 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
         k_w4a16_mma<G, 4><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;
-    k_gemv_reduce<<<(unsigned)((M * N + 31) / 32), 256, 0, st>>>(part, p.ksplit, (int)(M * N), Y);
+    if (p.ksplit <= 8) {
+        const int64_t n4 = M * N / 4;   // N % 8 == 0
+        k_part_reduce4<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((const floatx4*)part, p.ksplit, n4, (uint2*)Y);
+    } else {
+        k_gemv_reduce<<<(unsigned)((M * N + 31) / 32), 256, 0, st>>>(part, p.ksplit, (int)(M * N), Y);
+    }
     return hipGetLastError();
 }
 }  // namespace
