@@ -247,7 +247,7 @@ int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mea
  *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes, no initialization
  *   needed: for M = 1 the float32 split-K partials (the size may be 0); for M > 1 also x/s as
  *   bf16 in matrix-core operand order and its per-group sums (about 2*M*K bytes).
- * Requires N % 8 == 0 and at most 65535 * 64 rows.
+ * Requires N % 8 == 0, at most 65535 * 64 rows and, for M > 1, K <= 65535 * 256.
  */
 size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size);
 int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes,

@@ -239,7 +239,7 @@ int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t
         !aligned(zeros, 16) || !aligned(Y_bf16, 16))
         return AWQ_ERR_INVALID_ARG;
     const awq::GemmPlan p = awq::plan_gemm(M, K, N, group_size);
-    if (p.grid_y > 65535 || (N + 63) / 64 > kIntMax || p.mpad * (K / 8) / 256 > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (p.grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535)) return AWQ_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
     return hip_status(awq::launch_gemm((const uint16_t*)X_bf16, M, s, codes, scales, zeros, K, N, group_size,
                                        (uint16_t*)Y_bf16, workspace, p, (hipStream_t)stream));

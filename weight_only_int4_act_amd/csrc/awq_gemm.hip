@@ -32,44 +32,62 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
 // where sum_k x'_k adds the same bf16-rounded values, and the accumulator of a group starts at
 // -(128 + z) sum x' so that the products complete it.
 
-// x' = bf16(x / s) in A-operand order and its group sums.  Thread t owns row m = t / (K/8) and the
-// 8 channels 8*kb .. 8*kb+7 (kb = t % (K/8)); it writes them as the 16 bytes lane 16*(kb%4) + m%16
-// of fragment (m/16, kb/4) feeds to the matrix core:
-//   Xp[((m/16) * (K/32) + kb/4) * 64 + 16*(kb%4) + m%16] = pairs (x'_{8kb+j}, x'_{8kb+j+4}), j < 4.
-// The G/8 consecutive threads of one group add their sums with a fixed butterfly; the first writes
-// Sg[g * mpad + m].  Rows m in [M, mpad) are zero.
+// x' = bf16(x / s) in A-operand order and its group sums.  Workgroup (x, y) takes row block x (16
+// rows) and 256 channels y (8 K chunks: 8 KB of fragments that lie next to each other in Xp).  Thread
+// (row ml + 8h, kb) reads the 8 channels 8*kb .. 8*kb+7 of its row (a row's 32 threads read 512
+// contiguous bytes) and forms the 16 bytes that lane 16*(kb%4) + m%16 of fragment (m/16, kb/4)
+// feeds to the matrix core:
+//   Xp[((m/16) * (K/32) + kb/4) * 64 + 16*(kb%4) + m%16] = pairs (x'_{8kb+j}, x'_{8kb+j+4}), j < 4;
+// the entries meet in LDS and leave as contiguous 16-byte stores.  The G/8 consecutive threads of
+// one group add their sums with a fixed butterfly; the first writes Sg[g * mpad + m].  Rows m in
+// [M, mpad) are zero.
 template <int G>
 __global__ __launch_bounds__(256) void k_prep_x(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                 const float* __restrict__ s, int64_t mpad, u32x4* __restrict__ Xp,
                                                 float* __restrict__ Sg) {
-    const int64_t kbs = K / 8;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool live = t < mpad * kbs;            // the grid is rounded up to whole workgroups
-    const int64_t tt = live ? t : 0;
-    const int64_t m = tt / kbs, kb = tt % kbs;
-    float x[8];
-    if (live && m < M) {
-        const u32x4 xv = *(const u32x4*)(X + m * K + 8 * kb);
-        const floatx4 s0 = *(const floatx4*)(s + 8 * kb);
-        const floatx4 s1 = *(const floatx4*)(s + 8 * kb + 4);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const float sl = h < 2 ? s0[2 * h] : s1[2 * h - 4];
-            const float sh = h < 2 ? s0[2 * h + 1] : s1[2 * h - 3];
-            x[2 * h] = (float)(__bf16)(bf16_lo(xv[h]) / sl);
-            x[2 * h + 1] = (float)(__bf16)(bf16_hi(xv[h]) / sh);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    __shared__ u32x4 tile[512];
+    const int kbl = threadIdx.x & 31, ml = threadIdx.x >> 5;
+    const int64_t kbs = K / 8, kchunks = K / 32;
+    const int64_t kb = (int64_t)blockIdx.y * 32 + kbl;
+    const int64_t rb = blockIdx.x;
+    const bool kvalid = kb < kbs;
+    floatx4 s0 = floatx4{1.f, 1.f, 1.f, 1.f}, s1 = s0;
+    if (kvalid) {
+        s0 = *(const floatx4*)(s + 8 * kb);
+        s1 = *(const floatx4*)(s + 8 * kb + 4);
     }
-    float sx = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
 #pragma unroll
-    for (int o = 1; o < G / 8; o <<= 1) sx += __shfl_xor(sx, o, 64);
-    if (!live) return;
-    Xp[((m >> 4) * (K / 32) + (kb >> 2)) * 64 + 16 * (kb & 3) + (m & 15)] =
-        u32x4{pack_bf16x2(x[0], x[4]), pack_bf16x2(x[1], x[5]), pack_bf16x2(x[2], x[6]), pack_bf16x2(x[3], x[7])};
-    if (kb % (G / 8) == 0) Sg[(kb / (G / 8)) * mpad + m] = sx;
+    for (int h = 0; h < 2; ++h) {
+        const int mi = ml + 8 * h;
+        const int64_t m = rb * 16 + mi;
+        float x[8];
+        if (kvalid && m < M) {
+            const u32x4 xv = *(const u32x4*)(X + m * K + 8 * kb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sl = e < 2 ? s0[2 * e] : s1[2 * e - 4];
+                const float sh = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
+                x[2 * e] = (float)(__bf16)(bf16_lo(xv[e]) / sl);
+                x[2 * e + 1] = (float)(__bf16)(bf16_hi(xv[e]) / sh);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        float sx = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+#pragma unroll
+        for (int o = 1; o < G / 8; o <<= 1) sx += __shfl_xor(sx, o, 64);
+        tile[(kbl >> 2) * 64 + 16 * (kbl & 3) + mi] =
+            u32x4{pack_bf16x2(x[0], x[4]), pack_bf16x2(x[1], x[5]), pack_bf16x2(x[2], x[6]), pack_bf16x2(x[3], x[7])};
+        if (kvalid && kb % (G / 8) == 0) Sg[(kb / (G / 8)) * mpad + m] = sx;
+    }
+    __syncthreads();
+    const int64_t base = (rb * kchunks + (int64_t)blockIdx.y * 8) * 64;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = (int)threadIdx.x + 256 * h;
+        if ((int64_t)blockIdx.y * 8 + e / 64 < kchunks) Xp[base + e] = tile[e];
+    }
 }
 
 // Workgroup: 4 wavefronts over the same 16*MB rows x 64 columns, splitting the workgroup's groups
@@ -426,8 +444,8 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
     u32x4* Xp = (u32x4*)(base + p.off_xp);
     float* Sg = (float*)(base + p.off_sg);
     float* part = (float*)(base + p.off_part);
-    const int64_t threads = p.mpad * (K / 8);
-    k_prep_x<G><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(X, M, K, s, p.mpad, Xp, Sg);
+    // row blocks along x (up to 2^31 - 1), 256-channel blocks along y (K <= 16.7M)
+    k_prep_x<G><<<dim3((unsigned)(p.mpad / 16), (unsigned)((K + 255) / 256)), 256, 0, st>>>(X, M, K, s, p.mpad, Xp, Sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
