@@ -138,7 +138,7 @@ def cpu_baseline(layer, n_cols):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the AWQ path here runs on one GPU; run with --gpus 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
 
