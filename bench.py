@@ -128,9 +128,19 @@ def cpu_baseline(layer, n_cols):
     _, m = O.act_stats(X)
     res = O.search(X, W, m, layer.group_size, layer.zero_point, 21)
     dt = time.perf_counter() - t0
+    # the rest of the step, timed beside it: packing at the chosen scales and the W4A16 reference
+    # product at M = 1, 16 and 256
+    t1 = time.perf_counter()
+    s_best = O.scale_table(m, 21)[int(res["best"])]
+    w, d, z = O.pack(W, s_best, layer.group_size, layer.zero_point)
+    t2 = time.perf_counter()
+    for M in (1, 16, 256):
+        O.w4a16_ref(X[:M], s_best, w, d, z, layer.group_size)
+    t3 = time.perf_counter()
     flops = 21 * 2.0 * T * K * n_cols
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3), "best_alpha_index": int(res["best"]),
+            "seconds": round(dt, 3), "pack_seconds": round(t2 - t1, 3), "w4a16_ref_seconds": round(t3 - t2, 3),
+            "best_alpha_index": int(res["best"]),
             "sample": f"oracle (numpy float64) statistic + 21-alpha search of the 4096x4096 layer restricted to "
                       f"its first {n_cols} of 4096 output columns, all 8192 tokens ({flops / 1e12:.3f} TFLOP)"}
 
