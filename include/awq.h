@@ -144,6 +144,9 @@ int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_t
  * dequantized in registers, X E_i runs on bf16 matrix cores with float32 accumulation,
  * and only sum-of-squares partials leave the kernel.  Losses are exact sums of those
  * float32 products; they agree with a float64 evaluation to about 1e-3 relative.
+ * Size limits (AWQ_ERR_INVALID_ARG beyond them): T * K < 2^31; the scale table, its
+ * reciprocals and the float32 copy of W (about 4 K N bytes) within 4 GiB, i.e. K N up to
+ * about 1.07e9 (K = 8192: N up to ~131000); a 640-row tile of X (1280 K bytes) below 2^31.
  */
 size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg);
 int awq_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, int64_t N,
