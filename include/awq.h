@@ -206,6 +206,7 @@ int awq_clip_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K
  *   order of the float64 sums);  best  int32 [1] out;  s_best  float32 [K] out.
  *   workspace >= awq_search_multi_workspace_size(T, K, n_w, N, cfg) bytes (0 for bad sizes).
  * Each W_j is padded to a multiple of 16 columns with zeros, which quantize exactly.
+ * awq_search's size limits apply with N the sum of the padded column counts.
  */
 #define AWQ_MAX_PROJECTIONS 16
 size_t awq_search_multi_workspace_size(int64_t T, int64_t K, int32_t n_w, const int64_t* N,
