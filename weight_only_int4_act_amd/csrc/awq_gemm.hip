@@ -235,6 +235,178 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
     }
 }
 
+// Buffer resource over a byte range (accesses beyond it read zero) and a 16-byte-per-lane direct
+// transfer into LDS (buffer_load_dwordx4 ... lds, M0 = LDS base, saved and restored around it).
+namespace {
+typedef int gi32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ gi32x4 grsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return gi32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, 0x00020000};
+}
+// 16 bytes per active lane from byte offset voff of the resource to LDS address lds + 16*lane
+__device__ __forceinline__ void gdma16(gi32x4 rsrc, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
+}
+__device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+}  // namespace
+
+// M > 32: 64 rows (4 row blocks) x 256 columns per workgroup.  The 4 wavefronts walk the same K
+// groups, each with its own 64 columns (lane (r16, q) of wavefront w owns columns
+// n0 = 256*bx + 64*w + 4*r16 .. n0 + 3, as above), so the x' fragments and x' sums of a group are
+// copied once per workgroup straight into LDS by direct buffer-to-LDS transfers and read by all
+// four (double buffered: the next group's transfers are in flight while the current group's
+// products run).  Each wavefront keeps the code words, steps and zeros of its next group in a
+// second register buffer.  Every barrier first waits for all of the wavefront's memory operations,
+// so the transfers of the buffer it publishes have landed.
+template <int G>
+__global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restrict__ Xp, const float* __restrict__ Sg,
+                                                       int64_t mpad, int64_t M, const uint32_t* __restrict__ codes,
+                                                       const float* __restrict__ scales,
+                                                       const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
+                                                       uint16_t* __restrict__ Y, float* __restrict__ part) {
+    constexpr int C = G / 32, MB = 4;
+    constexpr int NE = MB * C * 64;              // 16-byte x' entries of a group (MB row blocks x C chunks)
+    constexpr int PT = NE / 256;                 // entries per thread (C of them)
+    __shared__ u32x4 xs[2][NE];
+    __shared__ floatx4 ss[2][MB * 4];            // x' sums of the group's 64 rows
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * 256 + 64 * wave + 4 * r16;
+    const bool nvalid = n0 < N;                  // N % 8 == 0: n0 < N implies n0 + 3 < N
+    const int64_t nc = nvalid ? n0 : 0;
+    const int64_t R0 = (int64_t)blockIdx.y * MB;  // first 16-row block
+    const int64_t n_groups = K / G, kchunks = K / 32;
+    const int64_t gpk = (n_groups + gridDim.z - 1) / gridDim.z;
+    const int64_t gb = min((int64_t)blockIdx.z * gpk, n_groups);
+    const int64_t ge = min(gb + gpk, n_groups);
+
+    uint32_t nib;
+    asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(nib));
+    const uint32_t bf128 = __builtin_amdgcn_readfirstlane(0x43004300u);
+    floatx4 acc[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // workgroup-shared x' of a group: entry e = (mb * C + c) * 64 + l is lane l's fragment of row
+    // block R0 + mb, chunk g*C + c; wavefront w's i-th transfer fills entries 256 i + 64 w .. + 63,
+    // and lanes 0-15 of wavefront 0 bring the sums of rows 4 lane .. 4 lane + 3
+    const gi32x4 xrs = grsrc(Xp, (uint32_t)(mpad / 16 * kchunks * 1024));
+    const gi32x4 srs = grsrc(Sg, (uint32_t)(n_groups * mpad * 4));
+    const uint32_t xs_lds = (uint32_t)(uintptr_t)&xs[0][0];
+    const uint32_t ss_lds = (uint32_t)(uintptr_t)&ss[0][0];
+    auto xdma = [&](int64_t g, int buf) {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i;
+            const int mb = e / (C * 64), c = (e / 64) % C, l = e % 64;
+            gdma16(xrs, (uint32_t)((((R0 + mb) * kchunks + g * C + c) * 64 + l) * 16),
+                   xs_lds + (uint32_t)((buf * NE + 256 * i + 64 * wave) * 16));
+        }
+        if (wave == 0 && lane < MB * 4)
+            gdma16(srs, (uint32_t)((g * mpad + R0 * 16 + 4 * lane) * 4), ss_lds + (uint32_t)(buf * MB * 4 * 16));
+    };
+    struct Buf {
+        u32x4 cw[C];
+        floatx4 dsc;
+        uint32_t zw;
+    };
+    auto issue = [&](int64_t g, Buf& b) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) b.cw[c] = *(const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc);
+        b.dsc = *(const floatx4*)(scales + g * N + nc);
+        b.zw = *(const uint32_t*)(zeros + g * N + nc);
+    };
+    auto consume = [&](const Buf& b, int buf) {
+        floatx4 accg[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const floatx4 sv = ss[buf][mb * 4 + q];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float off = -(128.f + (float)((b.zw >> (8 * j)) & 0xFFu));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accg[mb][j][i] = off * sv[i];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            u32x4 a[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) a[mb] = xs[buf][(mb * C + c) * 64 + lane];
+            const u32x4 cw = b.cw[c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 bo = u32x4{(cw[j] & nib) | bf128, ((cw[j] >> 4) & nib) | bf128,
+                                       ((cw[j] >> 8) & nib) | bf128, ((cw[j] >> 12) & nib) | bf128};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, bo),
+                                               accg[mb][j]);
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(b.dsc[j], accg[mb][j][i], acc[mb][j][i]);
+    };
+    // one group per step: while the products of group g run (from xs[g & 1]), the loads of group
+    // g + 1 are in flight (x' into the other LDS buffer, codes into the other register buffer)
+    Buf b0, b1;
+    if (gb < ge) {
+        xdma(gb, 0);
+        issue(gb, b0);
+    }
+    full_barrier();
+    for (int64_t g = gb; g < ge; g += 2) {
+        const bool n1 = g + 1 < ge;
+        if (n1) {
+            xdma(g + 1, 1);
+            issue(g + 1, b1);
+        }
+        consume(b0, 0);
+        full_barrier();                           // xs[1] filled, xs[0] no longer read
+        if (!n1) break;
+        const bool n2 = g + 2 < ge;
+        if (n2) {
+            xdma(g + 2, 0);
+            issue(g + 2, b0);
+        }
+        consume(b1, 1);
+        full_barrier();                           // xs[0] filled, xs[1] no longer read
+    }
+
+    if (!nvalid) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = (R0 + mb) * 16 + 4 * q + i;
+            if (m >= M) continue;
+            if (gridDim.z == 1) {
+                const uint32_t lo = pack_bf16x2(acc[mb][0][i], acc[mb][1][i]);
+                const uint32_t hi = pack_bf16x2(acc[mb][2][i], acc[mb][3][i]);
+                *(uint2*)(Y + m * N + n0) = uint2{lo, hi};
+            } else {
+                *(floatx4*)(part + ((int64_t)blockIdx.z * M + m) * N + n0) =
+                    floatx4{acc[mb][0][i], acc[mb][1][i], acc[mb][2][i], acc[mb][3][i]};
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
 // HBM-bound: every byte of packed weights is read once.  A workgroup owns 256 output columns and
 // 4*GPW quantization groups (G rows each): wavefront w takes groups 4i + w, i < GPW, of them.  Each
@@ -453,8 +625,10 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
         k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     else if (p.variant == 2)
         k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
-    else
+    else if (p.variant == 4)
         k_w4a16_mma<G, 4><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+    else
+        k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;
     if (p.ksplit <= 8) {
@@ -485,17 +659,24 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
         p.ws_bytes = p.grid_y > 1 ? (size_t)p.grid_y * N * sizeof(float) : 0;
         return p;
     }
-    // 16-row blocks per wavefront: as many as the rows need, up to 4 (64 rows x 64 columns)
-    p.variant = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    const int64_t rows = 16 * p.variant;
+    // 16-row blocks per wavefront: as many as the rows need, up to 4.  Variants 1, 2, 4: 64
+    // columns per workgroup, its wavefronts splitting the groups (k_w4a16_mma); variant 5 (M > 32
+    // when x' and its sums lie within the 32-bit byte range of a buffer resource): 64 rows x 256
+    // columns, x' shared through LDS (k_w4a16_mma_lds)
+    const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    const int64_t rows = 16 * mb;
     p.mpad = (M + rows - 1) / rows * rows;
-    p.grid_x = (N + 63) / 64;
+    const bool lds_ok = p.mpad * K * (int64_t)sizeof(uint16_t) < ((int64_t)1 << 32) &&
+                        n_groups * p.mpad * (int64_t)sizeof(float) < ((int64_t)1 << 32);
+    p.variant = mb == 4 && lds_ok ? 5 : mb;
+    p.grid_x = p.variant == 5 ? (N + 255) / 256 : (N + 63) / 64;
     p.grid_y = p.mpad / rows;
-    // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping at least
-    // one group per wavefront and the partials' index range within int
+    // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping enough
+    // groups per workgroup and the partials' index range within int
     const int64_t tiles = p.grid_x * p.grid_y;
     int64_t ks = 1;
-    while (tiles * ks < 512 && 2 * ks * 4 <= n_groups && 2 * ks * M * N < ((int64_t)1 << 31)) ks *= 2;
+    const int64_t min_groups = p.variant == 5 ? 2 : 4;   // two (one prefetched) or one per wavefront
+    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks * M * N < ((int64_t)1 << 31)) ks *= 2;
     p.grid_z = ks;
     p.ksplit = (int)ks;
     size_t off = 0;

@@ -86,7 +86,7 @@ hipError_t launch_greedy(const uint16_t* W, int64_t K, int64_t N, const float* m
 
 // ---- a6: W4A16 product
 struct GemmPlan {
-    int variant;             // 0: M = 1 GEMV; else row blocks of 16 per wavefront (1, 2 or 4)
+    int variant;             // 0: M = 1 GEMV; 1, 2, 4: row blocks of 16 per wavefront; 5: LDS-shared x' (M > 32)
     int64_t grid_x, grid_y, grid_z;
     int ksplit;              // workgroups along K (float32 partials added by a second kernel)
     int64_t mpad;            // M rounded up to the workgroup's row tile
