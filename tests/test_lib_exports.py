@@ -159,3 +159,114 @@ def test_binding_refuses_host_tensors(awq):
     X = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         awq.awq_act_stats(X, torch.zeros(128, dtype=torch.float64), False, 4, None, torch.zeros(8, dtype=torch.uint8))
+
+
+def test_gemm_rejects_misaligned_workspace(awq):
+    lib = awq.library()
+    p = ctypes.c_void_p(256)
+    need = awq.awq_w4a16_gemm_workspace_size(1, 8192, 8192, 128)
+    assert need > 0
+    assert lib.awq_w4a16_gemm(p, 1, p, p, p, p, 8192, 8192, 128, p, ctypes.c_void_p(256 + 16), need,
+                              None) == awq.AWQ_ERR_INVALID_ARG
+    assert lib.awq_w4a16_gemm(p, 1, p, p, p, p, 8192, 8192, 128, p, p, need - 1, None) == awq.AWQ_ERR_WORKSPACE
+
+
+def test_gemm_workspace_sizes(awq):
+    # M <= 16: partials and counters only when K is split; M > 16 adds x/s in operand order
+    for M in (1, 7, 16):
+        assert awq.awq_w4a16_gemm_workspace_size(M, 8192, 8192, 128) >= 4 * M * 8192 * 2
+    assert awq.awq_w4a16_gemm_workspace_size(256, 8192, 8192, 128) >= 256 * 8192 * 2
+    assert awq.awq_w4a16_gemm_workspace_size(1, 8192, 8192, 96) == 0
+
+
+def _host(nbytes, fill=0xA5):
+    buf = (ctypes.c_uint8 * nbytes)()
+    ctypes.memset(buf, fill, nbytes)
+    return buf
+
+
+def test_rejected_calls_write_nothing(awq):
+    """Every rejected call returns before anything is enqueued: buffers passed as outputs (host
+    memory here, never dereferenced by the library on these paths) keep their contents."""
+    lib = awq.library()
+    outs = [_host(4096) for _ in range(6)]
+    before = [bytes(b) for b in outs]
+    P = [ctypes.cast(b, ctypes.c_void_p) for b in outs]
+    src = ctypes.c_void_p(256)
+    cfg = awq.qconfig(128, True, 21)
+    bad_cfg = awq.qconfig(96, True, 21)
+    big = ctypes.c_size_t(1 << 40)
+    calls = [
+        lib.awq_act_stats(src, 8, 16, P[0], 2, 8, P[1], P[2], big, None),
+        lib.awq_act_max(src, 8, 16, P[0], 5, P[1], big, None),
+        lib.awq_scale_table(P[0], 16, 1, P[1], None),
+        lib.awq_scale_table_ex(P[0], None, 16, 21, 3, P[1], None),
+        lib.awq_weight_mean_abs(src, 0, 16, P[0], None),
+        lib.awq_search(src, 8, src, 128, 16, src, ctypes.byref(bad_cfg), P[0], big, P[1], P[2], P[3], None),
+        lib.awq_search_table(src, 8, src, 100, 16, src, ctypes.byref(cfg), P[0], big, P[1], P[2], P[3], None),
+        lib.awq_clip_search(src, 8, src, 128, 16, src, ctypes.byref(cfg), ctypes.c_float(0.0), P[0], big, P[1],
+                            P[2], P[3], None),
+        lib.awq_pack(src, 128, 16, src, ctypes.byref(bad_cfg), P[0], P[1], P[2], None),
+        lib.awq_w4a16_gemm(src, 1, src, src, src, src, 128, 12, 128, P[0], P[1], big, None),
+        lib.awq_w4a16_gemm(src, 1, src, src, src, src, 8192, 8192, 128, P[0], P[1], 16, None),
+        lib.awq_greedy_search(src, 256, 40, src, ctypes.byref(cfg), 20, 0, P[0], big, P[1], P[2], P[3], None),
+    ]
+    assert all(st < 0 for st in calls), calls
+    assert [bytes(b) for b in outs] == before
+
+
+def test_binding_checks_shapes_and_dtypes_before_launch(awq):
+    """The binding refuses mis-shaped or wrongly typed companions of a call (which the C ABI
+    cannot see) before anything reaches the device; CPU tensors show that no launch happens."""
+    import torch
+    K, N, g, M = 256, 64, 128, 4
+    bf, f32 = torch.bfloat16, torch.float32
+    X = torch.zeros(M, K, dtype=bf)
+    s = torch.ones(K, dtype=f32)
+    codes = torch.zeros(K // 8, N, dtype=torch.int32)
+    scales = torch.ones(K // g, N, dtype=f32)
+    zeros = torch.zeros(K // g, N, dtype=torch.uint8)
+    Y = torch.zeros(M, N, dtype=bf)
+    ws = torch.zeros(8, dtype=torch.uint8)
+
+    def gemm(**kw):
+        a = dict(X=X, s=s, codes=codes, scales=scales, zeros=zeros, group_size=g, Y=Y, ws=ws)
+        a.update(kw)
+        with pytest.raises(ValueError) as e:
+            awq.awq_w4a16_gemm(**a)
+        return str(e.value)
+
+    assert "X must be" in gemm(X=X.float())
+    assert "s must have shape" in gemm(s=torch.ones(K + 8, dtype=f32))
+    assert "codes must" in gemm(codes=torch.zeros(K // 8, N, dtype=torch.int64))
+    assert "scales must have shape" in gemm(scales=torch.ones(K // 64, N, dtype=f32))
+    assert "zeros must be" in gemm(zeros=zeros.int())
+    assert "Y must have shape" in gemm(Y=torch.zeros(M, N + 8, dtype=bf))
+    assert "multiple of the group size" in gemm(group_size=96)
+    assert "device tensors" in gemm()      # every shape right: only the device check is left
+
+    cfg = awq.qconfig(g, True, 21)
+    W = torch.zeros(K, N, dtype=bf)
+    m = torch.ones(K, dtype=f32)
+    losses = torch.zeros(21, dtype=torch.float64)
+    best = torch.zeros(1, dtype=torch.int32)
+    sb = torch.zeros(K, dtype=f32)
+    for bad in (dict(losses=torch.zeros(20, dtype=torch.float64)), dict(best=torch.zeros(1, dtype=torch.int64)),
+                dict(s_best=torch.zeros(K - 8, dtype=f32)), dict(W=torch.zeros(K + 8, N, dtype=bf)),
+                dict(mean_abs=m.double())):
+        a = dict(X=X, W=W, mean_abs=m, cfg=cfg, ws=ws, losses=losses, best=best, s_best=sb)
+        a.update(bad)
+        with pytest.raises(ValueError, match="must|is \\["):
+            awq.awq_search(**a)
+    with pytest.raises(ValueError, match="zeros must"):
+        awq.awq_pack(W, s, cfg, codes, scales, zeros.float())
+    with pytest.raises(ValueError, match="s_table must"):
+        awq.awq_scale_table(m, 21, torch.zeros(20, K, dtype=f32))
+    with pytest.raises(ValueError, match="sum_abs must"):
+        awq.awq_act_stats(X, torch.zeros(K, dtype=f32), False, M, None, ws)
+    with pytest.raises(ValueError, match="losses_each must"):
+        awq.awq_search_multi(X, [W, W], m, cfg, ws, losses, torch.zeros(3, 21, dtype=torch.float64), best, sb)
+    with pytest.raises(ValueError, match="err must"):
+        awq.awq_greedy_search(W, m, cfg, 20, 3, ws, sb, None, torch.zeros(K // g + 1, dtype=torch.float64))
+    with pytest.raises(ValueError, match="output must"):
+        awq.awq_clip_search(X, W, s, cfg, 0.5, ws, losses, best, torch.zeros(2, dtype=f32))

@@ -93,6 +93,39 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
+_CODE_DTYPES = tuple(d for d in (torch.int32, getattr(torch, "uint32", None)) if d is not None)
+
+
+def _expect(fn: str, name: str, t: Optional[torch.Tensor], dtypes, shape, optional: bool = False) -> None:
+    """Refuse a tensor whose dtype or shape differs from what the C entry point will assume: the
+    C ABI receives only pointers and the sizes taken from the other arguments, so a mis-shaped
+    buffer would otherwise be read or written out of bounds on the device."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{fn}: {name} is required")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{fn}: {name} must have shape {tuple(int(v) for v in shape)}, got {tuple(t.shape)}")
+
+
+def _matrix(fn: str, name: str, t: torch.Tensor, dtype=torch.bfloat16):
+    if t.dim() != 2:
+        raise ValueError(f"{fn}: {name} must be a matrix, got shape {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{fn}: {name} must be {dtype}, got {t.dtype}")
+    return t.shape
+
+
+def _group_rows(fn: str, K: int, g: int) -> int:
+    if g <= 0 or K % g or K % 8:
+        raise ValueError(f"{fn}: K = {K} must be a multiple of the group size {g} and of 8")
+    return K // g
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -120,7 +153,8 @@ def _nbytes(t: Optional[torch.Tensor]) -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """Zero-filled device scratch of at least ``nbytes`` bytes (256-byte aligned by torch)."""
+    """Zero-filled device scratch of at least ``nbytes`` bytes (256-byte aligned by torch).  Zero
+    filling is what awq_w4a16_gemm's arrival counters need before their first use."""
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
@@ -131,13 +165,17 @@ def awq_act_stats_workspace_size(T: int, K: int) -> int:
 
 def awq_act_stats(X: torch.Tensor, sum_abs: torch.Tensor, accumulate: bool, total_tokens: int,
                   mean_abs: Optional[torch.Tensor], ws: torch.Tensor, stream=None) -> None:
-    T, K = X.shape
+    T, K = _matrix("awq_act_stats", "X", X)
+    _expect("awq_act_stats", "sum_abs", sum_abs, torch.float64, (K,))
+    _expect("awq_act_stats", "mean_abs", mean_abs, torch.float32, (K,), optional=True)
     _check("awq_act_stats", _lib.awq_act_stats(_ptr(X), T, K, _ptr(sum_abs), 1 if accumulate else 0,
                                                int(total_tokens), _ptr(mean_abs), _ptr(ws), _nbytes(ws),
                                                _stream(stream)))
 
 
 def awq_scale_table(mean_abs: torch.Tensor, n_grid: int, s_table: torch.Tensor, stream=None) -> None:
+    _expect("awq_scale_table", "mean_abs", mean_abs, torch.float32, (mean_abs.numel(),))
+    _expect("awq_scale_table", "s_table", s_table, torch.float32, (n_grid, mean_abs.numel()))
     _check("awq_scale_table", _lib.awq_scale_table(_ptr(mean_abs), mean_abs.numel(), int(n_grid),
                                                    _ptr(s_table), _stream(stream)))
 
@@ -146,36 +184,57 @@ def awq_search_workspace_size(T: int, K: int, N: int, cfg: awq_qconfig) -> int:
     return int(_lib.awq_search_workspace_size(T, K, N, ctypes.byref(cfg)))
 
 
+def _search_outputs(fn: str, X, W, vec, vec_shape, cfg, losses, best, out, out_shape):
+    T, K = _matrix(fn, "X", X)
+    K2, N = _matrix(fn, "W", W)
+    if K2 != K:
+        raise ValueError(f"{fn}: X is [T, {K}] but W is [{K2}, N]")
+    _expect(fn, "scales", vec, torch.float32, vec_shape)
+    _expect(fn, "losses", losses, torch.float64, (cfg.n_grid,))
+    _expect(fn, "best", best, torch.int32, (1,))
+    _expect(fn, "output", out, torch.float32, out_shape)
+    return T, K, N
+
+
 def awq_search(X: torch.Tensor, W: torch.Tensor, mean_abs: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
                losses: torch.Tensor, best: torch.Tensor, s_best: torch.Tensor, stream=None) -> None:
-    T, K = X.shape
-    K2, N = W.shape
-    if K2 != K:
-        raise ValueError(f"X is [T, {K}] but W is [{K2}, N]")
+    T, K, N = _search_outputs("awq_search", X, W, mean_abs, (X.shape[-1],), cfg, losses, best, s_best,
+                              (X.shape[-1],))
     _check("awq_search", _lib.awq_search(_ptr(X), T, _ptr(W), K, N, _ptr(mean_abs), ctypes.byref(cfg), _ptr(ws),
                                          _nbytes(ws), _ptr(losses), _ptr(best), _ptr(s_best), _stream(stream)))
 
 
 def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, codes: torch.Tensor, scales: torch.Tensor,
              zeros: torch.Tensor, stream=None) -> None:
-    K, N = W.shape
+    K, N = _matrix("awq_pack", "W", W)
+    ng = _group_rows("awq_pack", K, cfg.group_size)
+    _expect("awq_pack", "s", s, torch.float32, (K,))
+    _expect("awq_pack", "codes", codes, _CODE_DTYPES, (K // 8, N))
+    _expect("awq_pack", "scales", scales, torch.float32, (ng, N))
+    _expect("awq_pack", "zeros", zeros, torch.uint8, (ng, N))
     _check("awq_pack", _lib.awq_pack(_ptr(W), K, N, _ptr(s), ctypes.byref(cfg), _ptr(codes), _ptr(scales),
                                      _ptr(zeros), _stream(stream)))
 
 
 def awq_act_max(X: torch.Tensor, max_abs: torch.Tensor, accumulate: bool, ws: torch.Tensor, stream=None) -> None:
-    T, K = X.shape
+    T, K = _matrix("awq_act_max", "X", X)
+    _expect("awq_act_max", "max_abs", max_abs, torch.float32, (K,))
     _check("awq_act_max", _lib.awq_act_max(_ptr(X), T, K, _ptr(max_abs), 1 if accumulate else 0, _ptr(ws),
                                            _nbytes(ws), _stream(stream)))
 
 
 def awq_weight_mean_abs(W: torch.Tensor, w_mean: torch.Tensor, stream=None) -> None:
-    K, N = W.shape
+    K, N = _matrix("awq_weight_mean_abs", "W", W)
+    _expect("awq_weight_mean_abs", "w_mean", w_mean, torch.float32, (K,))
     _check("awq_weight_mean_abs", _lib.awq_weight_mean_abs(_ptr(W), K, N, _ptr(w_mean), _stream(stream)))
 
 
 def awq_scale_table_ex(stat: torch.Tensor, w_mean: Optional[torch.Tensor], n_grid: int, normalize: bool,
                        s_table: torch.Tensor, stream=None) -> None:
+    K = stat.numel()
+    _expect("awq_scale_table_ex", "stat", stat, torch.float32, (K,))
+    _expect("awq_scale_table_ex", "w_mean", w_mean, torch.float32, (K,), optional=True)
+    _expect("awq_scale_table_ex", "s_table", s_table, torch.float32, (n_grid, K))
     _check("awq_scale_table_ex", _lib.awq_scale_table_ex(_ptr(stat), _ptr(w_mean) if w_mean is not None else None,
                                                          stat.numel(), int(n_grid), 1 if normalize else 0,
                                                          _ptr(s_table), _stream(stream)))
@@ -183,10 +242,8 @@ def awq_scale_table_ex(stat: torch.Tensor, w_mean: Optional[torch.Tensor], n_gri
 
 def awq_search_table(X: torch.Tensor, W: torch.Tensor, s_table: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
                      losses: torch.Tensor, best: torch.Tensor, s_best: torch.Tensor, stream=None) -> None:
-    T, K = X.shape
-    K2, N = W.shape
-    if K2 != K or tuple(s_table.shape) != (cfg.n_grid, K):
-        raise ValueError(f"shapes: X [T, {K}], W [{K2}, N], s_table {tuple(s_table.shape)} (want [{cfg.n_grid}, {K}])")
+    T, K, N = _search_outputs("awq_search_table", X, W, s_table, (cfg.n_grid, X.shape[-1]), cfg, losses, best,
+                              s_best, (X.shape[-1],))
     _check("awq_search_table", _lib.awq_search_table(_ptr(X), T, _ptr(W), K, N, _ptr(s_table), ctypes.byref(cfg),
                                                      _ptr(ws), _nbytes(ws), _ptr(losses), _ptr(best), _ptr(s_best),
                                                      _stream(stream)))
@@ -195,10 +252,7 @@ def awq_search_table(X: torch.Tensor, W: torch.Tensor, s_table: torch.Tensor, cf
 def awq_clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, cfg: awq_qconfig, clip_min: float,
                     ws: torch.Tensor, losses: torch.Tensor, best: torch.Tensor, clip_best: torch.Tensor,
                     stream=None) -> None:
-    T, K = X.shape
-    K2, N = W.shape
-    if K2 != K:
-        raise ValueError(f"X is [T, {K}] but W is [{K2}, N]")
+    T, K, N = _search_outputs("awq_clip_search", X, W, s, (X.shape[-1],), cfg, losses, best, clip_best, (1,))
     _check("awq_clip_search", _lib.awq_clip_search(_ptr(X), T, _ptr(W), K, N, _ptr(s), ctypes.byref(cfg),
                                                    float(clip_min), _ptr(ws), _nbytes(ws), _ptr(losses),
                                                    _ptr(best), _ptr(clip_best), _stream(stream)))
@@ -211,8 +265,15 @@ def awq_w4a16_gemm_workspace_size(M: int, K: int, N: int, group_size: int) -> in
 def awq_w4a16_gemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                    zeros: torch.Tensor, group_size: int, Y: torch.Tensor, ws: Optional[torch.Tensor],
                    stream=None) -> None:
-    M, K = X.shape
-    N = codes.shape[1]
+    fn = "awq_w4a16_gemm"
+    M, K = _matrix(fn, "X", X)
+    _, N = _matrix(fn, "codes", codes, codes.dtype if codes.dtype in _CODE_DTYPES else torch.int32)
+    ng = _group_rows(fn, K, int(group_size))
+    _expect(fn, "s", s, torch.float32, (K,))
+    _expect(fn, "codes", codes, _CODE_DTYPES, (K // 8, N))
+    _expect(fn, "scales", scales, torch.float32, (ng, N))
+    _expect(fn, "zeros", zeros, torch.uint8, (ng, N))
+    _expect(fn, "Y", Y, torch.bfloat16, (M, N))
     _check("awq_w4a16_gemm", _lib.awq_w4a16_gemm(_ptr(X), M, _ptr(s), _ptr(codes), _ptr(scales), _ptr(zeros),
                                                  K, N, int(group_size), _ptr(Y), _ptr(ws), _nbytes(ws),
                                                  _stream(stream)))
@@ -282,10 +343,17 @@ def awq_search_multi_workspace_size(T: int, K: int, Ns, cfg: awq_qconfig) -> int
 def awq_search_multi(X: torch.Tensor, Ws, mean_abs: torch.Tensor, cfg: awq_qconfig, ws: torch.Tensor,
                      losses: torch.Tensor, losses_each: Optional[torch.Tensor], best: torch.Tensor,
                      s_best: torch.Tensor, stream=None) -> None:
-    T, K = X.shape
+    fn = "awq_search_multi"
+    T, K = _matrix(fn, "X", X)
     for W in Ws:
-        if W.dim() != 2 or W.shape[0] != K:
-            raise ValueError(f"X is [T, {K}] but a projection is {tuple(W.shape)}")
+        if _matrix(fn, "W", W)[0] != K:
+            raise ValueError(f"{fn}: X is [T, {K}] but a projection is {tuple(W.shape)}")
+    _expect(fn, "mean_abs", mean_abs, torch.float32, (K,))
+    _expect(fn, "losses", losses, torch.float64, (cfg.n_grid,))
+    _expect(fn, "losses_each", losses_each, torch.float64, (len(Ws), cfg.n_grid), optional=True)
+    _expect(fn, "best", best, torch.int32, (1,))
+    _expect(fn, "s_best", s_best, torch.float32, (K,))
+    for W in Ws:
         _ptr(W)
     N, P = _host_arrays([W.shape[1] for W in Ws], Ws)
     _check("awq_search_multi", _lib.awq_search_multi(_ptr(X), T, len(Ws), P, N, K, _ptr(mean_abs),
@@ -327,7 +395,13 @@ def awq_greedy_workspace_size(K: int, N: int, cfg: awq_qconfig, n_cand: int = 20
 def awq_greedy_search(W: torch.Tensor, mean_abs: torch.Tensor, cfg: awq_qconfig, n_cand: int, passes: int,
                       ws: torch.Tensor, s_best: torch.Tensor, err_rtn: Optional[torch.Tensor] = None,
                       err: Optional[torch.Tensor] = None, stream=None) -> None:
-    K, N = W.shape
+    fn = "awq_greedy_search"
+    K, N = _matrix(fn, "W", W)
+    ng = _group_rows(fn, K, cfg.group_size)
+    _expect(fn, "mean_abs", mean_abs, torch.float32, (K,))
+    _expect(fn, "s_best", s_best, torch.float32, (K,))
+    _expect(fn, "err_rtn", err_rtn, torch.float64, (ng,), optional=True)
+    _expect(fn, "err", err, torch.float64, (ng,), optional=True)
     _check("awq_greedy_search", _lib.awq_greedy_search(_ptr(W), K, N, _ptr(mean_abs), ctypes.byref(cfg), int(n_cand),
                                                        int(passes), _ptr(ws), _nbytes(ws), _ptr(s_best),
                                                        _ptr(err_rtn), _ptr(err), _stream(stream)))
