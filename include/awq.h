@@ -248,10 +248,18 @@ int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mea
  * on chip and multiplied with 16-bit activations).
  *   X  bf16 [M, K];  s  float32 [K];  codes/scales/zeros as written by awq_pack;
  *   Y  bf16 [M, N] out.  Accumulation is float32; x/s is rounded to bf16 once.
- *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes, no initialization
- *   needed: for M = 1 the float32 split-K partials (the size may be 0); for M > 1 also x/s as
- *   bf16 in matrix-core operand order and its per-group sums (about 2*M*K bytes).
- * Requires N % 8 == 0, at most 65535 * 64 rows and, for M > 1, K <= 65535 * 256.
+ *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes (the size may be 0),
+ *   256-byte aligned.  Its first 64 KiB hold the arrival counters of the M = 1 product (one
+ *   32-bit counter per 256 output columns): they must be ZERO before the first call that uses
+ *   the workspace (a zero-filled allocation), this function writes nothing else there and every
+ *   completed call leaves them zero, so one workspace serves any sequence of calls of any shape
+ *   without clearing (re-zero it after using the memory for anything else).  After them: M = 1
+ *   (decode-shaped, one kernel per call) the float32 split-K partials; M > 1 the float32 split-K
+ *   partials, x/s as bf16 in matrix-core operand order and its per-group sums (about 2*M*K
+ *   bytes).  Calls that share a workspace must be ordered (same stream).
+ * Requires N % 8 == 0, K < 2^31, N <= 4194304, at most 65535 * 64 rows, for M > 1
+ * K <= 65535 * 256 and, for M > 32, M * K * 2 bytes of x/s below 4 GiB (AWQ_ERR_INVALID_ARG
+ * otherwise).
  */
 size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size);
 int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes,

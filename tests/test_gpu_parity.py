@@ -102,7 +102,7 @@ def test_gemm_and_closure(name):
     L, X64, W64, g, zp, ng, gpu, s, m, S, Lo = _case(name)
     q = gpu["q"]
     T = X64.shape[0]
-    for M in sorted({1, 7, 16, 37, min(T, 256), T}):
+    for M in sorted({1, 7, 16, min(T, 24), 37, min(T, 256), T}):
         Y = gpu_gemm(L.X[:M].contiguous(), q)
         Yr = O.w4a16_ref(X64[:M], gpu["s_best"], gpu["codes"], gpu["scales"], gpu["zeros"], g)
         err = rel_fro(Y, Yr)

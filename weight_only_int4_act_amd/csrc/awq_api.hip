@@ -238,9 +238,14 @@ int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t
     if (!aligned(X_bf16, 16) || !aligned(s, 16) || !aligned(codes, 16) || !aligned(scales, 16) ||
         !aligned(zeros, 16) || !aligned(Y_bf16, 16))
         return AWQ_ERR_INVALID_ARG;
+    if (K > kIntMax || N > (int64_t)(awq::kGemmCounterBytes / 4) * 256) return AWQ_ERR_INVALID_ARG;
     const awq::GemmPlan p = awq::plan_gemm(M, K, N, group_size);
-    if (p.grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535)) return AWQ_ERR_INVALID_ARG;
+    if (p.variant < 0 || p.grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535))
+        return AWQ_ERR_INVALID_ARG;
+    // M = 1: the split-K partials are addressed with 32-bit byte offsets (a buffer resource)
+    if (p.variant == 0 && p.ksplit * N * 4 > (int64_t)0xffffffff) return AWQ_ERR_INVALID_ARG;
     if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
+    if (p.ws_bytes && !aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_gemm((const uint16_t*)X_bf16, M, s, codes, scales, zeros, K, N, group_size,
                                        (uint16_t*)Y_bf16, workspace, p, (hipStream_t)stream));
 }

@@ -90,8 +90,8 @@ __global__ __launch_bounds__(256) void k_prep_x(const uint16_t* __restrict__ X, 
     }
 }
 
-// Workgroup: 4 wavefronts over the same 16*MB rows x 64 columns, splitting the workgroup's groups
-// of K between them (wavefront w takes groups gb + w, gb + w + 4, ...); a fixed-order sum through
+// 2..32 rows.  Workgroup: 4 wavefronts over the same 16*MB rows x 64 columns (MB = 1 for up to 16
+// rows, 2 for up to 32), splitting the workgroup's groups of K between them (wavefront w takes groups gb + w, gb + w + 4, ...); a fixed-order sum through
 // LDS joins them.  Lane (r16, q) owns the 4 adjacent columns n0 = 64*bx + 4*r16 .. n0 + 3 (one
 // 16-byte code load per code row) and uses column n0 + j as column r16 of its j-th 16-column
 // matrix-core tile; its accumulators hold rows 4q .. 4q+3 of each 16-row block.  With ksplit > 1
@@ -126,10 +126,9 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // For MB <= 2 the code words, steps, zeros and x' sums of this wavefront's next group (and, for
-    // MB = 1, its x' fragments) are loaded before the current group's products are issued (two
-    // register buffers), so a group's memory reads are in flight during the previous group's
-    // matrix work; with 4 row blocks the accumulators leave no room for a second buffer.
+    // The code words, steps, zeros and x' sums of this wavefront's next group (and, for MB = 1, its
+    // x' fragments) are loaded before the current group's products are issued (two register
+    // buffers), so a group's memory reads are in flight during the previous group's matrix work.
     constexpr bool XB = MB == 1;
     struct Buf {
         u32x4 cw[C];
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(b.dsc[j], accg[mb][j][i], acc[mb][j][i]);
     };
-    if constexpr (MB <= 2) {
+    {
         // two groups per step, so each buffer keeps a fixed set of registers
         Buf b0, b1;
         if (gb + wave < ge) issue(gb + wave, b0);
@@ -199,12 +198,6 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                 if (g + 8 < ge) issue(g + 8, b0);
                 consume(g + 4, b1);
             }
-        }
-    } else {
-        for (int64_t g = gb + wave; g < ge; g += 4) {
-            Buf b;
-            issue(g, b);
-            consume(g, b);
         }
     }
 
@@ -409,40 +402,62 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
 // HBM-bound: every byte of packed weights is read once.  A workgroup owns 256 output columns and
-// 4*GPW quantization groups (G rows each): wavefront w takes groups 4i + w, i < GPW, of them.  Each
-// lane reads 4 adjacent columns x 8 rows of codes with one 16-byte load per code row (a
-// wavefront reads 1 KB of one code row: fully coalesced); the loads of the next group are issued
-// before the current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values
-// 128 + q with one shift and one and-or, and v_dot2c_f32_bf16 multiplies them with the pair
-// (x'_k, x'_{k+4}) of activations x' = bf16(x/s) staged in LDS in that pair order.  The offset
-// and the zero point come out once per group: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x',
-// where sum x' adds the same bf16-rounded values the products used.  The 4 wavefronts reduce
-// through LDS in a fixed order; workgroups along K write float32 partials with plain stores and a
-// second small kernel adds them in a fixed order and writes the bf16 outputs.  (A
-// last-arriving-workgroup handoff inside one kernel would need device-scope release/acquire,
-// which on this multi-die GPU writes back and invalidates a whole L2 per workgroup.)  No atomics:
-// results are deterministic.
+// 4*GPW slices of VG rows of K: wavefront w takes slices 4i + w, i < GPW.  Each lane reads 4
+// adjacent columns x 8 rows of codes with one 16-byte streaming load per code row (a wavefront
+// reads 1 KB of one code row: fully coalesced); the loads of the next slice are issued before the
+// current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values 128 + q with
+// one shift and one and-or, and v_dot2c_f32_bf16 multiplies them with the pair (x'_k, x'_{k+4})
+// of activations x' = bf16(x/s) staged in LDS in that pair order.  The offset and the zero point
+// come out once per slice: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x', where sum x'
+// adds the same bf16-rounded values the products used.  Wavefronts 1-3 hand their sums to
+// wavefront 0 through LDS and leave; wavefront 0 adds them in a fixed order.  With one K block it
+// writes Y.  Otherwise it writes the workgroup's float32 partial with agent-scope stores
+// (written through to the device-coherent level, not left in one die's L2), waits for them and
+// bumps the column block's arrival counter with one agent-scope atomic; the wavefront that
+// arrives last reads every partial of the block with agent-scope loads, adds them in K-block
+// order (so the result does not depend on the arrival order), writes Y and sets the counter back
+// to zero.  No wavefront waits on another workgroup, and there are no floating-point atomics.
+#ifndef AWQ_GEMV_MAX_KSPLIT
+#define AWQ_GEMV_MAX_KSPLIT 16      // most K blocks (arrivals at one counter) of the M = 1 product
+#endif
+
+namespace {
+// float32 x4 to / from the device-coherent level: buffer operations with the agent-scope
+// cache-policy bit (sc1), so a partial written on one die is read back on another.
+constexpr int kCpolAgent = 16;
+constexpr int kCpolStream = 2;   // non-temporal: data read once
+__device__ __forceinline__ void store4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolAgent);
+}
+__device__ __forceinline__ floatx4 load4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolAgent));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+}  // namespace
+
 constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
 constexpr int kGemvWaves = 4;    // wavefronts per workgroup
-constexpr int kGemvGpw = 1;      // groups per wavefront
 
 // VG: rows a wavefront takes at a time, a divisor of the quantization group G.  Narrow layers
 // split each group into G/VG slices (each with the group's step and zero, and the sum of x' over
 // its own rows in the offset/zero correction, which is linear in the rows), so that more
 // workgroups share K and fill the GPU.
-template <int G, int VG>
+template <int G, int VG, int kGemvGpw>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
                                                     const uint32_t* __restrict__ codes,
                                                     const float* __restrict__ scales,
                                                     const uint8_t* __restrict__ zeros, int K, int N,
-                                                    uint16_t* __restrict__ Y, float* __restrict__ part) {
+                                                    uint16_t* __restrict__ Y, float* __restrict__ part,
+                                                    uint32_t* __restrict__ cnt) {
     static_assert(G % VG == 0 && VG >= 32, "slice of a group");
     constexpr int R = VG / 8;                    // code rows per slice
     constexpr int NG = kGemvWaves * kGemvGpw;    // slices per workgroup
     // x' of the workgroup's slices: slot i, code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
     __shared__ uint32_t xpair[NG][VG / 2];
     __shared__ float sxs[NG];
-    __shared__ float red[kGemvWaves][kGemvCols];
+    __shared__ floatx4 red[kGemvWaves - 1][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
     const int n_groups = K / VG;                 // slices, from here on called groups
@@ -546,18 +561,34 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
             consume(i + 1, b1);
         }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) red[wave][lane * 4 + c] = acc[c];
+    if (wave > 0) red[wave - 1][lane] = floatx4{acc[0], acc[1], acc[2], acc[3]};
     __syncthreads();
-    const int col = cb * kGemvCols + (int)threadIdx.x;
-    const float ps = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
-    if (col >= N) return;
+    if (wave > 0) return;
+    // wavefront 0, lane l: columns n0 .. n0 + 3 of the block
+    const floatx4 v = ((floatx4{acc[0], acc[1], acc[2], acc[3]} + red[0][lane]) + red[1][lane]) + red[2][lane];
     if (nkb == 1) {
-        const __bf16 o = (__bf16)ps;
-        Y[col] = __builtin_bit_cast(uint16_t, o);
-    } else {
-        part[(int64_t)kb * N + col] = ps;
+        if (nvalid) *(uint2*)(Y + n0) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        return;
     }
+    const __amdgpu_buffer_rsrc_t pr = rsrc(part, (uint32_t)((int64_t)nkb * N * 4));
+    if (nvalid) store4_agent(pr, (uint32_t)(((int64_t)kb * N + n0) * 4), v);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial has landed
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old != (uint32_t)(nkb - 1)) return;
+    // last arrival: the nkb partials of these columns in K-block order (loads of partials beyond
+    // nkb fall outside the resource and read zeros, so every load is issued unconditionally)
+    floatx4 t = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < nkb; b0 += 16) {
+        floatx4 p[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) p[u] = load4_agent(pr, (uint32_t)(((int64_t)(b0 + u) * N + n0) * 4));
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t += p[u];
+    }
+    if (nvalid) *(uint2*)(Y + n0) = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+    if (lane == 0) __hip_atomic_store(cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Y[n] = bf16(sum_b part[b][n]) in a fixed order.  A workgroup takes 32 columns; thread (c, l)
@@ -625,8 +656,6 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
         k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     else if (p.variant == 2)
         k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
-    else if (p.variant == 4)
-        k_w4a16_mma<G, 4><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     else
         k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
     e = hipGetLastError();
@@ -641,34 +670,47 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
 }
 }  // namespace
 
+// Every layout keeps the first kGemmCounterBytes of the workspace for the arrival counters of the
+// M <= 16 kernel and puts its data after them, so the counters (zero between calls) survive calls
+// of any shape that share one workspace.
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     GemmPlan p{};
     const int64_t n_groups = K / group_size;
     if (M == 1) {
+        // halve the rows a wavefront takes (down to 32) until there are ~1536 workgroups (about
+        // six per CU, so the last ones to finish leave little of the GPU idle), as long as the K
+        // split stays within AWQ_GEMV_MAX_KSPLIT: the arrivals of one column block's K blocks at
+        // its counter are serialized; beyond that, each wavefront takes 4 slices
         p.variant = 0;
         p.grid_x = (N + kGemvCols - 1) / kGemvCols;
-        // halve the rows a wavefront takes (down to 32) until there are ~1536 workgroups: about
-        // six per CU, enough that the last ones to finish leave little of the GPU idle
-        p.vgroup = group_size;
-        while (p.vgroup > 32 && p.grid_x * (K / p.vgroup) / (kGemvWaves * kGemvGpw) < 1536) p.vgroup /= 2;
-        const int64_t n_slices = K / p.vgroup;
-        p.grid_y = (n_slices + kGemvWaves * kGemvGpw - 1) / (kGemvWaves * kGemvGpw);
+        int64_t vg = group_size, gpw = 1;
+        while (vg > 32 && p.grid_x * (K / vg) / kGemvWaves < 1536 && K / (vg / 2) / kGemvWaves <= AWQ_GEMV_MAX_KSPLIT)
+            vg /= 2;
+        if ((K / vg + kGemvWaves - 1) / kGemvWaves > AWQ_GEMV_MAX_KSPLIT) gpw = 4;   // (two slices spill registers)
+        p.vgroup = (int)vg;
+        p.gpw = (int)gpw;
+        p.grid_y = (K / vg + kGemvWaves * gpw - 1) / (kGemvWaves * gpw);
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
         p.mpad = 1;
-        p.ws_bytes = p.grid_y > 1 ? (size_t)p.grid_y * N * sizeof(float) : 0;
+        p.off_cnt = 0;
+        p.off_part = kGemmCounterBytes;
+        p.ws_bytes = p.grid_y > 1 ? kGemmCounterBytes + align256((size_t)p.grid_y * N * sizeof(float)) : 0;
         return p;
     }
-    // 16-row blocks per wavefront: as many as the rows need, up to 4.  Variants 1, 2, 4: 64
-    // columns per workgroup, its wavefronts splitting the groups (k_w4a16_mma); variant 5 (M > 32
-    // when x' and its sums lie within the 32-bit byte range of a buffer resource): 64 rows x 256
-    // columns, x' shared through LDS (k_w4a16_mma_lds)
+    // 2..32 rows: 16 or 32 rows x 64 columns per workgroup, its wavefronts splitting the groups of
+    // K (k_w4a16_mma); more rows: 64 rows x 256 columns, x' shared through LDS (k_w4a16_mma_lds),
+    // which addresses x' and its sums through buffer resources (32-bit byte offsets)
     const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     const int64_t rows = 16 * mb;
     p.mpad = (M + rows - 1) / rows * rows;
     const bool lds_ok = p.mpad * K * (int64_t)sizeof(uint16_t) < ((int64_t)1 << 32) &&
                         n_groups * p.mpad * (int64_t)sizeof(float) < ((int64_t)1 << 32);
-    p.variant = mb == 4 && lds_ok ? 5 : mb;
+    if (mb == 4 && !lds_ok) {
+        p.variant = -1;   // unsupported size
+        return p;
+    }
+    p.variant = mb == 4 ? 5 : mb;
     p.grid_x = p.variant == 5 ? (N + 255) / 256 : (N + 63) / 64;
     p.grid_y = p.mpad / rows;
     // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping enough
@@ -679,7 +721,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks * M * N < ((int64_t)1 << 31)) ks *= 2;
     p.grid_z = ks;
     p.ksplit = (int)ks;
-    size_t off = 0;
+    size_t off = kGemmCounterBytes;   // the counter region is never used for data (see plan_gemm's M <= 16 case)
     p.off_part = off; off = align256(off + (ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0));
     p.off_xp = off;   off = align256(off + (size_t)p.mpad * K * sizeof(uint16_t));
     p.off_sg = off;   off = align256(off + (size_t)n_groups * p.mpad * sizeof(float));
@@ -687,28 +729,37 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     return p;
 }
 
+namespace {
+template <int G, int VG>
+void launch_gemv(const uint16_t* X, const float* s, const uint32_t* codes, const float* scales, const uint8_t* zeros,
+                 int64_t K, int64_t N, uint16_t* Y, float* part, uint32_t* cnt, const GemmPlan& p, hipStream_t st) {
+    dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
+    if (p.gpw == 1)
+        k_w4a16_gemv<G, VG, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+    else
+        k_w4a16_gemv<G, VG, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+}
+}  // namespace
+
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes,
                        const float* scales, const uint8_t* zeros, int64_t K, int64_t N, int group_size,
                        uint16_t* Y, void* ws, const GemmPlan& p, hipStream_t st) {
     if (p.variant == 0) {
-        float* part = (float*)((char*)ws + p.off_part);
-        dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
+        float* part = p.grid_y > 1 ? (float*)((char*)ws + p.off_part) : nullptr;
+        uint32_t* cnt = p.grid_y > 1 ? (uint32_t*)((char*)ws + p.off_cnt) : nullptr;
         const int vg = p.vgroup;
         if (group_size == 32)
-            k_w4a16_gemv<32, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            launch_gemv<32, 32>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         else if (group_size == 64 && vg == 64)
-            k_w4a16_gemv<64, 64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            launch_gemv<64, 64>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         else if (group_size == 64)
-            k_w4a16_gemv<64, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            launch_gemv<64, 32>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         else if (vg == 128)
-            k_w4a16_gemv<128, 128><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            launch_gemv<128, 128>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         else if (vg == 64)
-            k_w4a16_gemv<128, 64><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
+            launch_gemv<128, 64>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         else
-            k_w4a16_gemv<128, 32><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess || p.grid_y == 1) return e;
-        k_gemv_reduce<<<(unsigned)((N + 31) / 32), 256, 0, st>>>(part, (int)p.grid_y, (int)N, Y);
+            launch_gemv<128, 32>(X, s, codes, scales, zeros, K, N, Y, part, cnt, p, st);
         return hipGetLastError();
     }
     if (group_size == 32) return launch_mma<32>(X, M, s, codes, scales, zeros, K, N, Y, ws, p, st);

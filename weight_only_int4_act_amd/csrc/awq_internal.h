@@ -85,14 +85,21 @@ hipError_t launch_greedy(const uint16_t* W, int64_t K, int64_t N, const float* m
                          hipStream_t st);
 
 // ---- a6: W4A16 product
+// Arrival counters of the M <= 16 product: one uint32 per 256 output columns, at the start of
+// every W4A16 workspace (N up to 4194304 columns).
+constexpr size_t kGemmCounterBytes = 65536;
 struct GemmPlan {
-    int variant;             // 0: M = 1 GEMV; 1, 2, 4: row blocks of 16 per wavefront; 5: LDS-shared x' (M > 32)
+    int variant;             // 0: M = 1 GEMV; 1: 2..16 rows; 2: 17..32 rows; 5: LDS-shared x' (M > 32);
+                             // -1: size not supported
     int64_t grid_x, grid_y, grid_z;
-    int ksplit;              // workgroups along K (float32 partials added by a second kernel)
+    int ksplit;              // workgroups along K
     int64_t mpad;            // M rounded up to the workgroup's row tile
-    int vgroup;              // M = 1: rows of a group a wavefront takes at a time
-    // workspace layout (byte offsets): split-K partials, x' in fragment order, group sums of x'
-    size_t off_part, off_xp, off_sg, ws_bytes;
+    int vgroup;              // M = 1: rows of K a wavefront takes at a time (a slice of a group);
+                             // 2..16 rows: quantization groups of K per workgroup
+    int gpw;                 // M = 1: slices per wavefront
+    // workspace layout (byte offsets): split-K partials, arrival counters (M <= 16, zero between
+    // calls), x' in fragment order and group sums of x' (M > 16)
+    size_t off_part, off_cnt, off_xp, off_sg, ws_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size);
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const float* s, const uint32_t* codes,
