@@ -51,6 +51,7 @@ extern "C" {
                                     clip_ratio outside [0, 1] */
 #define AWQ_ERR_WORKSPACE (-3)   /* workspace smaller than the matching *_workspace_size() */
 #define AWQ_ERR_HIP (-4)         /* a HIP call failed; awq_last_hip_error() holds its code */
+#define AWQ_ERR_SCRATCH (-5)     /* awq_w4a16_gemm_noalloc: the call needs more than its fixed scratch */
 
 /* Quantization settings ([P4] 架构, AWQConfig; [P2] section 2, quant_config).
  *   w_bit       bits per weight; only 4 is supported.
@@ -266,6 +267,26 @@ int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t
                    const float* scales, const uint8_t* zeros, int64_t K, int64_t N,
                    int32_t group_size, void* Y_bf16, void* workspace, size_t ws_bytes,
                    void* stream);
+
+/* ---------------------------------------------------------------- a6 without allocation
+ * For callers that cannot allocate: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  awq_w4a16_gemm with the same arguments minus the workspace:
+ * the same kernels, the same results (bit for bit), the scratch taken from one fixed buffer per
+ * GPU that the library holds for the life of the process
+ * (awq_w4a16_gemm_static_scratch_bytes(): 16 MiB plus 64 KiB of arrival counters).  Nothing is
+ * allocated, freed or synchronized by the call.  The buffer is shared by every call on that GPU
+ * and keeps the last call's contents: calls that can overlap on one GPU (different streams or
+ * threads without ordering) race and must not be issued; order them on one stream.  The calling
+ * thread's current HIP device must be the device of `stream` (the buffer's device address is
+ * looked up once per device, on that device's first call).  A call whose workspace
+ * (awq_w4a16_gemm_workspace_size) exceeds the buffer returns AWQ_ERR_SCRATCH before anything is
+ * enqueued: M = 1 fits for N up to about 260000 columns; larger M fits when its partials, x/s and
+ * group sums do (for example M = 16 with K = N = 8192).
+ */
+size_t awq_w4a16_gemm_static_scratch_bytes(void);
+int awq_w4a16_gemm_noalloc(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes,
+                           const float* scales, const uint8_t* zeros, int64_t K, int64_t N,
+                           int32_t group_size, void* Y_bf16, void* stream);
 
 /* ---------------------------------------------------------------- status helpers */
 const char* awq_status_string(int status);

@@ -22,6 +22,7 @@ AWQ_ERR_INVALID_ARG = -1
 AWQ_ERR_UNSUPPORTED = -2
 AWQ_ERR_WORKSPACE = -3
 AWQ_ERR_HIP = -4
+AWQ_ERR_SCRATCH = -5
 AWQ_MAX_POW2_CANDIDATES = 32   # most power-of-two candidates of awq_greedy_search
 AWQ_MAX_PROJECTIONS = 16   # most matrices one awq_search_multi call takes
 
@@ -67,6 +68,8 @@ _SIGNATURES = {
     "awq_scale_table_ex": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P]),
     "awq_w4a16_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "awq_w4a16_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P, _SZ, _P]),
+    "awq_w4a16_gemm_static_scratch_bytes": (_SZ, []),
+    "awq_w4a16_gemm_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_last_hip_error": (ctypes.c_int, []),
     "awq_version": (ctypes.c_char_p, []),
@@ -277,6 +280,25 @@ def awq_w4a16_gemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scales
     _check("awq_w4a16_gemm", _lib.awq_w4a16_gemm(_ptr(X), M, _ptr(s), _ptr(codes), _ptr(scales), _ptr(zeros),
                                                  K, N, int(group_size), _ptr(Y), _ptr(ws), _nbytes(ws),
                                                  _stream(stream)))
+
+
+def awq_w4a16_gemm_static_scratch_bytes() -> int:
+    return int(_lib.awq_w4a16_gemm_static_scratch_bytes())
+
+
+def awq_w4a16_gemm_noalloc(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                           zeros: torch.Tensor, group_size: int, Y: torch.Tensor, stream=None) -> None:
+    fn = "awq_w4a16_gemm_noalloc"
+    M, K = _matrix(fn, "X", X)
+    _, N = _matrix(fn, "codes", codes, codes.dtype if codes.dtype in _CODE_DTYPES else torch.int32)
+    ng = _group_rows(fn, K, int(group_size))
+    _expect(fn, "s", s, torch.float32, (K,))
+    _expect(fn, "codes", codes, _CODE_DTYPES, (K // 8, N))
+    _expect(fn, "scales", scales, torch.float32, (ng, N))
+    _expect(fn, "zeros", zeros, torch.uint8, (ng, N))
+    _expect(fn, "Y", Y, torch.bfloat16, (M, N))
+    _check(fn, _lib.awq_w4a16_gemm_noalloc(_ptr(X), M, _ptr(s), _ptr(codes), _ptr(scales), _ptr(zeros), K, N,
+                                           int(group_size), _ptr(Y), _stream(stream)))
 
 
 def awq_status_string(status: int) -> str:

@@ -3,6 +3,8 @@
 #include "../../include/awq.h"
 #include "awq_internal.h"
 
+#include <mutex>
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -228,9 +230,14 @@ size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t gr
     return awq::plan_gemm(M, K, N, group_size).ws_bytes;
 }
 
-int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes, const float* scales,
-                   const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size, void* Y_bf16, void* workspace,
-                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of awq_w4a16_gemm's arguments other than the workspace; fills the plan.
+int check_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes, const float* scales,
+               const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size, const void* Y_bf16,
+               awq::GemmPlan* p) {
     if (!X_bf16 || !s || !codes || !scales || !zeros || !Y_bf16) return AWQ_ERR_INVALID_ARG;
     if (M <= 0 || K <= 0 || N <= 0 || N % 8 != 0) return AWQ_ERR_INVALID_ARG;
     if (!group_ok(group_size)) return AWQ_ERR_UNSUPPORTED;
@@ -239,15 +246,75 @@ int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t
         !aligned(zeros, 16) || !aligned(Y_bf16, 16))
         return AWQ_ERR_INVALID_ARG;
     if (K > kIntMax || N > (int64_t)(awq::kGemmCounterBytes / 4) * 256) return AWQ_ERR_INVALID_ARG;
-    const awq::GemmPlan p = awq::plan_gemm(M, K, N, group_size);
-    if (p.variant < 0 || p.grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535))
+    *p = awq::plan_gemm(M, K, N, group_size);
+    if (p->variant < 0 || p->grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535))
         return AWQ_ERR_INVALID_ARG;
     // M = 1: the split-K partials are addressed with 32-bit byte offsets (a buffer resource)
-    if (p.variant == 0 && p.ksplit * N * 4 > (int64_t)0xffffffff) return AWQ_ERR_INVALID_ARG;
+    if (p->variant == 0 && p->ksplit * N * 4 > (int64_t)0xffffffff) return AWQ_ERR_INVALID_ARG;
+    return AWQ_OK;
+}
+
+// The allocation-free entry point's scratch: one fixed array per GPU, held until the process
+// ends.  Host code never uses the array's name as an address (on the host it is only a stand-in
+// for the device symbol); its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.  It starts zeroed (the arrival counters at its
+// front must be zero) and every completed call leaves those counters zero.
+constexpr size_t kScratchBytes = awq::kGemmCounterBytes + ((size_t)16 << 20);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void* scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of this device's scratch (looked up on the device's first call); nullptr on a
+// HIP error (recorded for awq_last_hip_error).
+void* device_scratch(hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int awq_w4a16_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes, const float* scales,
+                   const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size, void* Y_bf16, void* workspace,
+                   size_t ws_bytes, void* stream) {
+    awq::GemmPlan p;
+    const int st = check_gemm(X_bf16, M, s, codes, scales, zeros, K, N, group_size, Y_bf16, &p);
+    if (st != AWQ_OK) return st;
     if (ws_bytes < p.ws_bytes || (p.ws_bytes && !workspace)) return AWQ_ERR_WORKSPACE;
     if (p.ws_bytes && !aligned(workspace, 256)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_gemm((const uint16_t*)X_bf16, M, s, codes, scales, zeros, K, N, group_size,
                                        (uint16_t*)Y_bf16, workspace, p, (hipStream_t)stream));
+}
+
+size_t awq_w4a16_gemm_static_scratch_bytes(void) { return kScratchBytes; }
+
+int awq_w4a16_gemm_noalloc(const void* X_bf16, int64_t M, const float* s, const uint32_t* codes,
+                           const float* scales, const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size,
+                           void* Y_bf16, void* stream) {
+    awq::GemmPlan p;
+    const int st = check_gemm(X_bf16, M, s, codes, scales, zeros, K, N, group_size, Y_bf16, &p);
+    if (st != AWQ_OK) return st;
+    if (p.ws_bytes > kScratchBytes) return AWQ_ERR_SCRATCH;
+    hipError_t e = hipSuccess;
+    void* ws = p.ws_bytes ? device_scratch(&e) : nullptr;
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(awq::launch_gemm((const uint16_t*)X_bf16, M, s, codes, scales, zeros, K, N, group_size,
+                                       (uint16_t*)Y_bf16, ws, p, (hipStream_t)stream));
 }
 
 const char* awq_status_string(int status) {
@@ -257,6 +324,9 @@ const char* awq_status_string(int status) {
         case AWQ_ERR_UNSUPPORTED: return "unsupported configuration (w_bit, group_size, n_grid or clip_ratio)";
         case AWQ_ERR_WORKSPACE: return "workspace too small";
         case AWQ_ERR_HIP: return "HIP runtime error (see awq_last_hip_error)";
+        case AWQ_ERR_SCRATCH:
+            return "the call needs more scratch than the fixed per-GPU buffer of awq_w4a16_gemm_noalloc "
+                   "(awq_w4a16_gemm_static_scratch_bytes); use awq_w4a16_gemm with a workspace";
         default: return "unknown status";
     }
 }
