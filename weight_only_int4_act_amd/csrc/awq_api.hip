@@ -18,6 +18,10 @@ int hip_status(hipError_t e) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 constexpr int64_t kIntMax = 0x7fffffff;
+constexpr int64_t kGemmRowsMax = (int64_t)65535 * 64;   // M: workgroup rows of the product's grid
+// every size is checked against these bounds before any arithmetic on it, so no size query or
+// plan can overflow
+bool in_range(int64_t v, int64_t hi) { return v > 0 && v <= hi; }
 
 int check_cfg(const awq_qconfig* cfg, int64_t K) {
     if (!cfg) return AWQ_ERR_INVALID_ARG;
@@ -35,13 +39,14 @@ int check_cfg(const awq_qconfig* cfg, int64_t K) {
 extern "C" {
 
 size_t awq_act_stats_workspace_size(int64_t T, int64_t K) {
-    if (T <= 0 || K <= 0) return 0;
+    if (!in_range(T, kIntMax) || !in_range(K, kIntMax)) return 0;
     return awq::plan_stats(T, K).ws_bytes;
 }
 
 int awq_act_stats(const void* X_bf16, int64_t T, int64_t K, double* sum_abs, int accumulate,
                   int64_t total_tokens, float* mean_abs, void* workspace, size_t ws_bytes, void* stream) {
-    if (!X_bf16 || !sum_abs || T <= 0 || K <= 0 || total_tokens < T) return AWQ_ERR_INVALID_ARG;
+    if (!X_bf16 || !sum_abs || !in_range(T, kIntMax) || !in_range(K, kIntMax) || total_tokens < T)
+        return AWQ_ERR_INVALID_ARG;
     if (accumulate != 0 && accumulate != 1) return AWQ_ERR_INVALID_ARG;
     if (!aligned(X_bf16, 16) || !aligned(sum_abs, 8) || (mean_abs && !aligned(mean_abs, 4)))
         return AWQ_ERR_INVALID_ARG;
@@ -53,7 +58,7 @@ int awq_act_stats(const void* X_bf16, int64_t T, int64_t K, double* sum_abs, int
 }
 
 int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_table, void* stream) {
-    if (!mean_abs || !s_table || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (!mean_abs || !s_table || !in_range(K, kIntMax)) return AWQ_ERR_INVALID_ARG;
     if (n_grid < 2 || n_grid > 64) return AWQ_ERR_UNSUPPORTED;
     if (!aligned(mean_abs, 4) || !aligned(s_table, 4)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_scale_table(mean_abs, K, n_grid, s_table, nullptr, (hipStream_t)stream));
@@ -61,7 +66,7 @@ int awq_scale_table(const float* mean_abs, int64_t K, int32_t n_grid, float* s_t
 
 int awq_act_max(const void* X_bf16, int64_t T, int64_t K, float* max_abs, int accumulate, void* workspace,
                 size_t ws_bytes, void* stream) {
-    if (!X_bf16 || !max_abs || T <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (!X_bf16 || !max_abs || !in_range(T, kIntMax) || !in_range(K, kIntMax)) return AWQ_ERR_INVALID_ARG;
     if (accumulate != 0 && accumulate != 1) return AWQ_ERR_INVALID_ARG;
     if (!aligned(X_bf16, 16) || !aligned(max_abs, 4)) return AWQ_ERR_INVALID_ARG;
     const awq::StatsPlan p = awq::plan_stats(T, K);
@@ -72,14 +77,14 @@ int awq_act_max(const void* X_bf16, int64_t T, int64_t K, float* max_abs, int ac
 }
 
 int awq_weight_mean_abs(const void* W_bf16, int64_t K, int64_t N, float* w_mean, void* stream) {
-    if (!W_bf16 || !w_mean || K <= 0 || N <= 0 || K > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (!W_bf16 || !w_mean || !in_range(K, kIntMax) || !in_range(N, kIntMax)) return AWQ_ERR_INVALID_ARG;
     if (!aligned(W_bf16, 2) || !aligned(w_mean, 4)) return AWQ_ERR_INVALID_ARG;
     return hip_status(awq::launch_weight_mean_abs((const uint16_t*)W_bf16, K, N, w_mean, (hipStream_t)stream));
 }
 
 int awq_scale_table_ex(const float* stat, const float* w_mean, int64_t K, int32_t n_grid, int32_t normalize,
                        float* s_table, void* stream) {
-    if (!stat || !s_table || K <= 0) return AWQ_ERR_INVALID_ARG;
+    if (!stat || !s_table || !in_range(K, kIntMax)) return AWQ_ERR_INVALID_ARG;
     if (n_grid < 2 || n_grid > 64) return AWQ_ERR_UNSUPPORTED;
     if (normalize != 0 && normalize != 1) return AWQ_ERR_INVALID_ARG;
     if (!aligned(stat, 4) || !aligned(s_table, 4) || (w_mean && !aligned(w_mean, 4))) return AWQ_ERR_INVALID_ARG;
@@ -88,7 +93,9 @@ int awq_scale_table_ex(const float* stat, const float* w_mean, int64_t K, int32_
 }
 
 size_t awq_search_workspace_size(int64_t T, int64_t K, int64_t N, const awq_qconfig* cfg) {
-    if (T <= 0 || K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
+    if (!in_range(T, kIntMax) || !in_range(K, kIntMax) || !in_range(N, kIntMax) || T * K > kIntMax ||
+        check_cfg(cfg, K) != AWQ_OK)
+        return 0;
     return awq::plan_search(T, K, N, cfg->group_size, cfg->zero_point, cfg->n_grid, false).ws_bytes;
 }
 
@@ -99,7 +106,8 @@ int check_search(const void* X_bf16, int64_t T, const void* W_bf16, int64_t K, i
                  const awq_qconfig* cfg, void* workspace, size_t ws_bytes, const double* losses, const int32_t* best,
                  const float* out, bool clip, awq::SearchPlan* p) {
     if (!X_bf16 || !W_bf16 || !vec || !losses || !best || !out) return AWQ_ERR_INVALID_ARG;
-    if (T <= 0 || K <= 0 || N <= 0 || T * K > kIntMax || N > kIntMax) return AWQ_ERR_INVALID_ARG;
+    if (!in_range(T, kIntMax) || !in_range(K, kIntMax) || !in_range(N, kIntMax) || T * K > kIntMax)
+        return AWQ_ERR_INVALID_ARG;
     int st = check_cfg(cfg, K);
     if (st != AWQ_OK) return st;
     if (!aligned(X_bf16, 16) || !aligned(W_bf16, 2) || !aligned(vec, 4) || !aligned(losses, 8) ||
@@ -164,7 +172,9 @@ size_t awq_search_multi_workspace_size(int64_t T, int64_t K, int32_t n_w, const 
         if (N[j] <= 0 || N[j] > kIntMax) return 0;
         cols += (N[j] + 15) / 16 * 16;
     }
-    if (T <= 0 || K <= 0 || check_cfg(cfg, K) != AWQ_OK) return 0;
+    if (!in_range(T, kIntMax) || !in_range(K, kIntMax) || T * K > kIntMax || cols > kIntMax ||
+        check_cfg(cfg, K) != AWQ_OK)
+        return 0;
     const bool clip = cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f;
     return awq::plan_search(T, K, cols, cfg->group_size, cfg->zero_point, cfg->n_grid, clip).ws_bytes;
 }
@@ -190,14 +200,16 @@ int awq_search_multi(const void* X_bf16, int64_t T, int32_t n_w, const void* con
 }
 
 size_t awq_greedy_workspace_size(int64_t K, int64_t N, const awq_qconfig* cfg, int32_t n_cand) {
-    if (K <= 0 || N <= 0 || check_cfg(cfg, K) != AWQ_OK || n_cand < 2 || n_cand > AWQ_MAX_POW2_CANDIDATES) return 0;
+    if (!in_range(K, kIntMax) || !in_range(N, kIntMax) || check_cfg(cfg, K) != AWQ_OK || n_cand < 2 ||
+        n_cand > AWQ_MAX_POW2_CANDIDATES || K / cfg->group_size > 65535)
+        return 0;
     return awq::plan_greedy(K, N, cfg->group_size, n_cand).ws_bytes;
 }
 
 int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mean_abs, const awq_qconfig* cfg,
                       int32_t n_cand, int32_t passes, void* workspace, size_t ws_bytes, float* s_best,
                       double* err_rtn, double* err, void* stream) {
-    if (!W_bf16 || !mean_abs || !s_best || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;
+    if (!W_bf16 || !mean_abs || !s_best || !in_range(K, kIntMax) || !in_range(N, kIntMax)) return AWQ_ERR_INVALID_ARG;
     int st = check_cfg(cfg, K);
     if (st != AWQ_OK) return st;
     if (cfg->clip_ratio > 0.f && cfg->clip_ratio < 1.f) return AWQ_ERR_UNSUPPORTED;
@@ -215,7 +227,8 @@ int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mea
 
 int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq_qconfig* cfg, uint32_t* codes,
              float* scales, uint8_t* zeros, void* stream) {
-    if (!W_bf16 || !s || !codes || !scales || !zeros || K <= 0 || N <= 0) return AWQ_ERR_INVALID_ARG;
+    if (!W_bf16 || !s || !codes || !scales || !zeros || !in_range(K, kIntMax) || !in_range(N, kIntMax))
+        return AWQ_ERR_INVALID_ARG;
     int st = check_cfg(cfg, K);
     if (st != AWQ_OK) return st;
     if (K / cfg->group_size > 65535) return AWQ_ERR_INVALID_ARG;
@@ -226,7 +239,9 @@ int awq_pack(const void* W_bf16, int64_t K, int64_t N, const float* s, const awq
 }
 
 size_t awq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int32_t group_size) {
-    if (M <= 0 || K <= 0 || N <= 0 || !group_ok(group_size) || K % group_size) return 0;
+    if (!in_range(M, kGemmRowsMax) || !in_range(K, kIntMax) || !in_range(N, (int64_t)(awq::kGemmCounterBytes / 4) * 256) ||
+        !group_ok(group_size) || K % group_size)
+        return 0;
     return awq::plan_gemm(M, K, N, group_size).ws_bytes;
 }
 
@@ -239,13 +254,14 @@ int check_gemm(const void* X_bf16, int64_t M, const float* s, const uint32_t* co
                const uint8_t* zeros, int64_t K, int64_t N, int32_t group_size, const void* Y_bf16,
                awq::GemmPlan* p) {
     if (!X_bf16 || !s || !codes || !scales || !zeros || !Y_bf16) return AWQ_ERR_INVALID_ARG;
-    if (M <= 0 || K <= 0 || N <= 0 || N % 8 != 0) return AWQ_ERR_INVALID_ARG;
+    if (!in_range(M, kGemmRowsMax) || !in_range(K, kIntMax) || !in_range(N, (int64_t)(awq::kGemmCounterBytes / 4) * 256) ||
+        N % 8 != 0)
+        return AWQ_ERR_INVALID_ARG;
     if (!group_ok(group_size)) return AWQ_ERR_UNSUPPORTED;
     if (K % group_size != 0) return AWQ_ERR_INVALID_ARG;
     if (!aligned(X_bf16, 16) || !aligned(s, 16) || !aligned(codes, 16) || !aligned(scales, 16) ||
         !aligned(zeros, 16) || !aligned(Y_bf16, 16))
         return AWQ_ERR_INVALID_ARG;
-    if (K > kIntMax || N > (int64_t)(awq::kGemmCounterBytes / 4) * 256) return AWQ_ERR_INVALID_ARG;
     *p = awq::plan_gemm(M, K, N, group_size);
     if (p->variant < 0 || p->grid_y > 65535 || (N + 63) / 64 > kIntMax || (M > 1 && (K + 255) / 256 > 65535))
         return AWQ_ERR_INVALID_ARG;
