@@ -239,8 +239,10 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": search_traffic(),
-                     "kernel": "awq_search call (k_search fused loss kernel + scale table, W tiling, loss "
-                               "reduction and argmin kernels)",
+                     "kernel": "awq_search call: k_search (the fused loss kernel, ~98% of the call) plus the "
+                               "scale table, W and X tiling, loss reduction and argmin kernels",
+                     "duration": "mean over the timed steps of HIP events recorded around each awq_search call "
+                                 "on the stream the library launches on",
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(search_ms, 4)},
         "best_alpha_index": int(best.item()),
     }

@@ -1,0 +1,97 @@
+"""GPU parity on the readings that random two-signed groups never reach.
+
+* One-signed groups: every weight of a column's group >= 0, or every one <= 0.  The asymmetric
+  range is widened to include 0 ("大模型 AWQ 量化实战" section 2, ``zero_point``; the reading that
+  keeps the zero a valid INT4 value), so such groups get zero 0 (all >= 0) or 15 (all <= 0);
+  the symmetric form is unaffected by the sign but still checked.  Search losses, the choice and
+  the packed codes, steps and zeros are compared with the oracle as in the main parity tests.
+* Alpha grids longer than the kernel's 7-alpha slices with a partial last slice (n_grid 33: five
+  slices, the last with 5 alphas; n_grid 64: ten, the last with 1), against the oracle's losses
+  over the same grid ("AWQ (Activation-aware Weight Quantization)", 缩放因子优化的完整流程 step 3
+  with alpha_i = i / (n_grid - 1)).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import awq_oracle as O
+from weight_only_int4_act_amd import inputs as I
+from tests.gpu_util import gpu_gemm, gpu_layer, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+def _one_signed(W, g, seed):
+    """Force the groups of some columns to one sign: (column + group) % 3 == 0 -> all >= 0,
+    == 1 -> all <= 0, otherwise left two-signed."""
+    w = I.bf16_to_f64(W).copy()
+    K, N = w.shape
+    for j in range(K // g):
+        for n in range(N):
+            r = (n + j) % 3
+            if r == 0:
+                w[j * g:(j + 1) * g, n] = np.abs(w[j * g:(j + 1) * g, n])
+            elif r == 1:
+                w[j * g:(j + 1) * g, n] = -np.abs(w[j * g:(j + 1) * g, n])
+    return I.to_bf16(w.astype(np.float32)), w
+
+
+def _check_layer(L_X, W_bf16, g, zp, ng, label):
+    X64 = I.bf16_to_f64(L_X)
+    W64 = I.bf16_to_f64(W_bf16)
+    gpu = gpu_layer(L_X, W_bf16, g, zp, ng)
+    _, m = O.act_stats(X64)
+    assert np.array_equal(gpu["mean_abs"], m)
+    S = O.scale_table(m, ng)
+    Lo = O.losses(X64, W64, S, g, zp)
+    rel = np.abs(gpu["losses"] - Lo) / np.maximum(Lo, 1e-300)
+    b = gpu["best"]
+    log(f"[edge] {label}: max rel L err {rel.max():.2e}, best gpu {b} oracle {O.select(Lo)}")
+    assert np.all(rel <= 1e-2), rel
+    assert Lo[b] <= 1.01 * Lo.min()
+    assert np.array_equal(gpu["s_best"], S[b])
+    w, d, z = O.pack(W64, S[b], g, zp)
+    P = S[b].astype(np.float64)[:, None] * W64
+    t, tz = O.pre_round_values(P, d, g, zp)
+    ties = O.near_tie(t) | np.repeat(O.near_tie(tz), g, axis=0)
+    bad = O.unpack_nibbles(w) != O.unpack_nibbles(gpu["codes"])
+    log(f"[edge] {label}: code mismatches {bad.sum()} (near-ties {ties.sum()})")
+    assert not np.any(bad & ~ties)
+    assert np.array_equal(gpu["scales"], d) and np.array_equal(gpu["zeros"], z)
+    return gpu, w, d, z
+
+
+@pytest.mark.parametrize("zp,g", [(True, 128), (False, 64), (True, 32)])
+def test_one_signed_groups(zp, g):
+    L = I.small(700, 384, 48, seed=21, group_size=g, zero_point=zp)
+    Wb, w = _one_signed(L.W, g, seed=21)
+    gpu, wq, d, z = _check_layer(L.X, Wb, g, zp, 21, f"one-signed zp={zp} g={g}")
+    K, N = w.shape
+    if zp:
+        # groups that are all >= 0 have zero 0, all <= 0 zero 15 (unless the group is all zero)
+        for j in range(K // g):
+            for n in range(N):
+                col = w[j * g:(j + 1) * g, n]
+                if np.all(col == 0):
+                    continue
+                if (n + j) % 3 == 0:
+                    assert gpu["zeros"][j, n] == 0
+                elif (n + j) % 3 == 1:
+                    assert gpu["zeros"][j, n] == 15
+    else:
+        assert np.all(gpu["zeros"] == 8)
+    # the packed layer still reproduces the product
+    Y = gpu_gemm(L.X[:16].contiguous(), gpu["q"])
+    Yr = O.w4a16_ref(I.bf16_to_f64(L.X[:16]), gpu["s_best"], gpu["codes"], gpu["scales"], gpu["zeros"], g)
+    assert rel_fro(Y, Yr) <= 2e-2
+
+
+@pytest.mark.parametrize("ng", [33, 64])
+def test_long_alpha_grids(ng):
+    L = I.small(1250, 256, 40, seed=30 + ng)
+    _check_layer(L.X, L.W, 128, True, ng, f"n_grid={ng}")
+
+
+def test_long_alpha_grid_symmetric():
+    L = I.small(600, 192, 24, seed=40, group_size=64, zero_point=False)
+    _check_layer(L.X, L.W, 64, False, 33, "n_grid=33 sym g=64")

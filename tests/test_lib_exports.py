@@ -270,3 +270,14 @@ def test_binding_checks_shapes_and_dtypes_before_launch(awq):
         awq.awq_greedy_search(W, m, cfg, 20, 3, ws, sb, None, torch.zeros(K // g + 1, dtype=torch.float64))
     with pytest.raises(ValueError, match="output must"):
         awq.awq_clip_search(X, W, s, cfg, 0.5, ws, losses, best, torch.zeros(2, dtype=f32))
+
+
+def test_gemm_rejects_sizes_beyond_buffer_addressing(awq):
+    # M > 32 stages x/s and its sums for buffer addressing: x/s at or above 4 GiB is rejected
+    lib = awq.library()
+    p = ctypes.c_void_p(256)
+    M, K, N = 262144, 8192, 64          # M K 2 bytes = 4 GiB
+    assert awq.awq_w4a16_gemm_workspace_size(M, K, N, 128) == 0
+    assert lib.awq_w4a16_gemm(p, M, p, p, p, p, K, N, 128, p, p, ctypes.c_size_t(1 << 40),
+                              None) == awq.AWQ_ERR_INVALID_ARG
+    assert awq.awq_w4a16_gemm_workspace_size(M - 64, K, N, 128) > 0   # just below the limit
