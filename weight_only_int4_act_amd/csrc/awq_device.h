@@ -11,6 +11,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kCusPerXcd = 32;
 
 // bf16 <-> f32 on raw bit patterns (exact widening; RNE narrowing handled by the compiler).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

@@ -19,13 +19,16 @@
 //   * Every wavefront keeps the bf16 X fragments of its rows for the current group in registers
 //     (read from a tiled copy of X, one group ahead) and reuses them for all NA alphas:
 //     acc[alpha][row block] += X_chunk . E_alpha_chunk on v_mfma_f32_16x16x32_bf16.
-//   * The inputs of the E computation (float32 W tile, scale and reciprocal rows) reach LDS by
+//   * The inputs of the E computation (bf16 W tile, scale and reciprocal rows) reach LDS by
 //     direct global->LDS transfers, three groups in flight.
 //   * Epilogue: sum of squares of the float32 accumulators, reduced in a fixed order to one
 //     float64 partial per (token tile, column tile, alpha).  A second kernel sums the partials
 //     in a fixed order and a third picks the first minimum.
 //   * Tile order is XCD-aware: the workgroups that run together on one XCD share a token tile,
-//     so that XCD's L2 serves the X panel to all of them.
+//     so that XCD's L2 serves the X panel to all of them.  Successive waves of workgroups on an
+//     XCD walk K in opposite directions, so each starts on the part of the panel the previous one
+//     left in L2, and the W tile (read by one column block's alpha slices only) streams through
+//     L2 with the non-temporal hint.
 // The quantizer inside the search is the float32 evaluation of the packing quantizer of
 // awq_pack (which evaluates it exactly in float64); the two differ only for elements whose
 // pre-round value lies within float32 rounding of a .5 boundary.
@@ -50,13 +53,14 @@ __device__ __forceinline__ int kmap(int c, int q) {
     else return 8 * q;
 }
 
-// W [K, N] bf16 -> Wt (float32): for column block nb (16 columns), chunk kc (32 channels), half h
-// and lane l, the 4 float32 values W[G*(kc/C) + kmap(kc%C, l/16) + 4h + e][16*nb + l%16], e < 4,
-// as one 16-byte word (so a lane reads its 8 values of a chunk as two linear 16-byte words).
-// Columns beyond N are zero (a zero column quantizes to zero error).
+// W [K, N] bf16 -> Wt (bf16, matrix-core B order): for column block nb (16 columns), chunk kc (32
+// channels) and lane l, the 8 values W[G*(kc/C) + kmap(kc%C, l/16) + e][16*nb + l%16], e < 8, as one
+// 16-byte word (value e in the low half of 32-bit word e/2 when e is even, in the high half when
+// odd), so that a lane reads its 8 values of a chunk as one linear 16-byte word.  Columns beyond N
+// are zero (a zero column quantizes to zero error).
 template <int G>
 __global__ __launch_bounds__(256) void k_tile_w(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                                int64_t total, floatx4* __restrict__ Wt) {
+                                                int64_t total, u32x4* __restrict__ Wt) {
     constexpr int C = G / 32;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one (nb, kc, lane)
     if (e >= total) return;
@@ -66,12 +70,10 @@ __global__ __launch_bounds__(256) void k_tile_w(const uint16_t* __restrict__ W, 
     const int64_t kc = rest % kchunks, nb = rest / kchunks;
     const int64_t k0 = (kc / C) * G + kmap<G>((int)(kc % C), lane >> 4);
     const int64_t n = nb * 16 + (lane & 15);
-    float v[8];
+    uint32_t v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = n < N ? bf16_lo((uint32_t)W[(k0 + i) * N + n]) : 0.f;
-    floatx4* dst = Wt + rest * 128 + lane;
-    dst[0] = floatx4{v[0], v[1], v[2], v[3]};
-    dst[64] = floatx4{v[4], v[5], v[6], v[7]};
+    for (int i = 0; i < 8; ++i) v[i] = n < N ? (uint32_t)W[(k0 + i) * N + n] : 0u;
+    Wt[e] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
 
 // X [T, K] bf16 -> Xt: for 16-row block R, chunk kc and lane l, the 16 bytes lane l feeds to the
@@ -179,6 +181,19 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
         : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "memory");
 }
+// The same with the non-temporal hint: the lines it brings into L2 are the first to be replaced.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
+}
 // Lane J of each 16-lane row of v, for every lane of that row (DPP row_newbcast, folded by the
 // compiler into the consuming VALU instruction as a source modifier).
 template <int J>
@@ -201,17 +216,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // scaled, codes clamped to the 16 levels); without it the range is the group's own.
 template <int G, int NA, int RBW, int NW, bool ZP, bool CLIP>
 __global__ __launch_bounds__(NW * 64, 1) void k_search(
-    const u32x4* __restrict__ Xt, int T, int K, const floatx4* __restrict__ Wt, int NB,
+    const u32x4* __restrict__ Xt, int T, int K, const u32x4* __restrict__ Wt, int NB,
     const float* __restrict__ s_tab, const float* __restrict__ inv_tab, const float* __restrict__ clip_tab,
     uint32_t stage_bytes, int n_grid, int n_asplit, int n_tiles, int tiles_per_xcd, double* __restrict__ partials) {
     constexpr int C = G / 32;            // K chunks per group
     constexpr int BM = NW * RBW * 16;    // token rows per workgroup
-    constexpr int NWE = C * 128;         // 16-byte W entries of a group tile (float32)
+    constexpr int NWE = C * 64;          // 16-byte W entries of a group tile (bf16)
     constexpr int NSE = NA * G / 4;      // 16-byte entries of NA scale rows of one group
     constexpr int SPAD = 2;              // entries between scale and reciprocal rows (LDS banks)
     constexpr int NSTG = NWE + 2 * NSE + SPAD;   // staged 16-byte entries per group
-    constexpr int NSTGP = 2 * NW * 64;   // staging entries incl. padding (two per thread)
-    static_assert(NW == 8 && NA < NW && NA >= NW / 2 && NSTG <= NSTGP, "tile shape");   // waves 0-3 always own a slot
+    constexpr int NT = (NSTG + NW * 64 - 1) / (NW * 64);   // staging transfers per thread and group
+    constexpr int NSTGP = NT * NW * 64;  // staging entries incl. padding
+    static_assert(NW == 8 && NA < NW && NA >= NW / 2 && NT <= 2, "tile shape");   // waves 0-3 always own a slot
 
     const int tile = xcd_tile(blockIdx.x, tiles_per_xcd);
     if (tile >= n_tiles) return;
@@ -224,11 +240,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     const int q = lane >> 4, r16 = lane & 15;
     const int n_groups = K / G;
     const int kchunks = K / 32;
+    // K order: the workgroups of one XCD run in waves of one per CU; every other wave walks the
+    // groups from the last to the first, so that it starts on the X panel the previous wave left in
+    // that XCD's L2.  The sum over K is the same up to float32 rounding order.
+    const bool rev = ((blockIdx.x / kNumXcd) / kCusPerXcd) & 1;
 
     // E tiles (bf16, B-operand layout), double buffered over groups.
     __shared__ u32x4 Es[2][NA][C][64];
     // Staged inputs of the E computation of one group, four groups deep (group g in Stg[g % 4]): the
-    // W tile (float32, in B-operand order), then NA scale rows, then NA reciprocal rows (16-byte
+    // W tile (bf16, in B-operand order), then NA scale rows, then NA reciprocal rows (16-byte
     // entries).
     __shared__ u32x4 Stg[4][NSTGP];
     __shared__ double red[NW][NA];
@@ -256,26 +276,29 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     constexpr bool X3 = C == 4;
     auto xslot = [](int c) { return X3 ? (c == 3 ? 0 : c) : c % XD; };
     u32x4 xr[XD][RBW];
-    // chunk kc (counted over the whole K range, clamped to the last one) into ring slot `slot`
-    auto load_X = [&](int kc, int slot) {
-        kc = min(kc, kchunks - 1);
+    // chunk c (compile-time, < C) of group g (counted in this workgroup's K order, clamped to the
+    // last group) into ring slot `slot`: the group and row block in the scalar offset, the chunk in
+    // the instruction's immediate field.
+    auto load_X = [&](int g, int c, int slot) {
+        g = min(g, n_groups - 1);
+        const uint32_t goff = (uint32_t)(rev ? n_groups - 1 - g : g) * (C * 1024);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
             xr[slot][rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         xrsrc, xvoff, (rb * kchunks + kc) * 1024, 0));
+                                                         xrsrc, xvoff + c * 1024, goff + (uint32_t)(rb * kchunks) * 1024, 0));
     };
 
-    // ---- staging of the E inputs of group jg: entry e (thread t copies e = t and e = t + 512,
-    // 2 transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  SPAD
+    // ---- staging of the E inputs of group jg: entry e (thread t copies e = t + 512 r, r < NT
+    // transfers) is a 16-byte piece of the W tile, of a scale row or of a reciprocal row.  SPAD
     // entries between the scale and the reciprocal rows shift the latter by 8 LDS banks (they hold
     // a copy of the first scale entry), and the entries past NSTG re-read the last valid entry.
     // The scale table, its reciprocals and the W tiles lie in one range of the workspace that
     // starts at s_tab (stage_bytes long, checked below 4 GB by the host); a transfer's source is a
     // byte offset in it that advances by a fixed step per group.
     const i32x4 srsrc = byte_rsrc(s_tab, stage_bytes);
-    uint32_t stg_off[2], stg_step[2];
+    uint32_t stg_off[NT], stg_step[NT];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NT; ++r) {
         const int e = min((int)threadIdx.x + NW * 64 * r, NSTG - 1);
         const int es = e - NWE;
         const int which = es >= NSE + SPAD;              // 0: scale row (or padding), 1: reciprocal row
@@ -283,8 +306,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int a = idx / (G / 4), off = (idx % (G / 4)) * 4;
         const char* src;
         if (e < NWE) {
-            src = (const char*)(Wt + (int64_t)nb * kchunks * 128 + e);
-            stg_step[r] = (uint32_t)(C * 128 * sizeof(floatx4));
+            src = (const char*)(Wt + (int64_t)nb * kchunks * 64 + e);
+            stg_step[r] = (uint32_t)(C * 64 * sizeof(u32x4));
         } else {
             src = (const char*)((which ? inv_tab : s_tab) + (int64_t)min(a0 + a, n_grid - 1) * K + off);
             stg_step[r] = (uint32_t)(G * sizeof(float));
@@ -293,10 +316,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     }
     const uint32_t stg_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&Stg[0][0]) +
                              (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
-    auto stage = [&](int jg, int buf) {
+    // NTW: this wavefront's first transfer is a W tile piece (with G = 128 the W tile is exactly
+    // the first transfer of wavefronts 0-3), issued with the non-temporal hint: the W tile is read by
+    // the few workgroups of its column block only, so it streams through L2 and leaves it to the X
+    // panel, which the other workgroups of the XCD re-read.
+    auto stage = [&](auto ntw_tag, int jg, int buf) {   // jg counted in this workgroup's K order
+        constexpr bool NTW = decltype(ntw_tag)::value;
+        const uint32_t jp = (uint32_t)(rev ? n_groups - 1 - jg : jg);
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-            dma16(srsrc, stg_off[r] + (uint32_t)jg * stg_step[r], stg_lds + (uint32_t)(buf * NSTGP + NW * 64 * r) * 16);
+        for (int r = 0; r < NT; ++r) {
+            const uint32_t src = stg_off[r] + jp * stg_step[r];
+            const uint32_t dst = stg_lds + (uint32_t)(buf * NSTGP + NW * 64 * r) * 16;
+            if (NTW && r == 0) dma16_nt(srsrc, src, dst);
+            else dma16(srsrc, src, dst);
+        }
     };
 
     // ---- E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].
@@ -319,12 +352,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // LDS read, and each multiply takes lane j's value of its row as a row_newbcast:j source.
     const int srow = NWE + (slot * G) / 4;   // this slot's scale row (16-byte entries)
     const int sidx = (r16 < 8 ? srow * 4 : (srow + NSE + SPAD) * 4) + (r16 & 7) + kmap<G>(0, q);
-    u32x4 in[2][2];                          // W halves of two chunks
+    u32x4 in[2];                             // W values (bf16 pairs) of two chunks
     float sv[C];                             // per chunk: this lane's scale or reciprocal
     auto fetch_in = [&](int ibuf, int c) {
         const u32x4* st = &Stg[ibuf][0];
-        in[c & 1][0] = st[c * 128 + lane];
-        in[c & 1][1] = st[c * 128 + 64 + lane];
+        in[c & 1] = st[c * 64 + lane];
         sv[c] = ((const float*)st)[sidx + kmap<G>(c, 0)];
     };
     // The first chunk's inputs are issued ahead of compute_E, inside a matrix-core half;
@@ -340,17 +372,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         float cmx[C], cmn[C];       // per-chunk range, combined below as a tree
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const floatx4 w0 = __builtin_bit_cast(floatx4, in[c & 1][0]);
-            const floatx4 w1 = __builtin_bit_cast(floatx4, in[c & 1][1]);
+            const u32x4 w = in[c & 1];
             float* v = &pk[c * 8];
-            v[0] = rowbcast<0>(sv[c]) * w0[0];
-            v[1] = rowbcast<1>(sv[c]) * w0[1];
-            v[2] = rowbcast<2>(sv[c]) * w0[2];
-            v[3] = rowbcast<3>(sv[c]) * w0[3];
-            v[4] = rowbcast<4>(sv[c]) * w1[0];
-            v[5] = rowbcast<5>(sv[c]) * w1[1];
-            v[6] = rowbcast<6>(sv[c]) * w1[2];
-            v[7] = rowbcast<7>(sv[c]) * w1[3];
+            v[0] = rowbcast<0>(sv[c]) * bf16_lo(w[0]);
+            v[1] = rowbcast<1>(sv[c]) * bf16_hi(w[0]);
+            v[2] = rowbcast<2>(sv[c]) * bf16_lo(w[1]);
+            v[3] = rowbcast<3>(sv[c]) * bf16_hi(w[1]);
+            v[4] = rowbcast<4>(sv[c]) * bf16_lo(w[2]);
+            v[5] = rowbcast<5>(sv[c]) * bf16_hi(w[2]);
+            v[6] = rowbcast<6>(sv[c]) * bf16_lo(w[3]);
+            v[7] = rowbcast<7>(sv[c]) * bf16_hi(w[3]);
             if (c + 2 < C) fetch_in(ibuf, c + 2);
             if (ZP) {
                 cmx[c] = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), fmaxf(v[6], v[7]));
@@ -421,10 +452,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     constexpr int XS = (SC + 1 + (X3 ? 1 : 0)) * RBW;
     // PRE: after the products of alpha NA-2 in the last chunk (when the other alphas' E fragments
     // are dead), issue the LDS reads of the first inputs of an E computation (staged in Stg[pbuf]).
-    auto mfma_group = [&](auto pre_tag, int jg, int buf, int sjg, int sbuf, int pbuf) {
+    auto mfma_group = [&](auto pre_tag, auto ntw_tag, int jg, int buf, int sjg, int sbuf, int pbuf) {
         constexpr bool PRE = decltype(pre_tag)::value;
         constexpr int PA = NA > 2 ? NA - 2 : 0;
-        if constexpr (X3) load_X(jg * C + 2, 2);
+        if constexpr (X3) load_X(jg, 2, 2);
         u32x4 B[NA];
 #pragma unroll
         for (int a = 0; a < NA; ++a) B[a] = Es[buf][a][0][lane];
@@ -442,11 +473,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
                 if (PRE && c == C - 1 && a == PA) prefetch_E(pbuf);
             }
             if constexpr (X3) {
-                if (c == 0) load_X(jg * C + 3, 0);
-                if (c == 1) load_X(jg * C + C + 1, 1);
-                if (c == 3) load_X(jg * C + C, 0);
+                if (c == 0) load_X(jg, 3, 0);
+                if (c == 1) load_X(jg + 1, 1, 1);
+                if (c == 3) load_X(jg + 1, 0, 0);
             } else {
-                load_X(jg * C + c + XD, c % XD);
+                load_X(jg + (c + XD) / C, (c + XD) % C, c % XD);
             }
             // issue order inside the chunk: per alpha, its RBW products then the next chunk's E
             // fragment read; the X reloads last.  Keeps one E fragment set and one X set live.
@@ -459,15 +490,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
             }
             if (!X3 || c != 2) __builtin_amdgcn_sched_group_barrier(0x020, RBW, 0);   // VMEM read
             __builtin_amdgcn_sched_barrier(0);
-            if (c == SC) stage(sjg, sbuf);
+            if (c == SC) stage(ntw_tag, sjg, sbuf);
         }
     };
 
     // ---- prologue: the first X chunks in registers, inputs of groups 0-3 staged, E(0) computed.
 #pragma unroll
-    for (int c = 0; c < (X3 ? 2 : XD); ++c) load_X(c, c);
+    for (int c = 0; c < (X3 ? 2 : XD); ++c) load_X(c / C, c % C, c);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) stage(min(g, n_groups - 1), g);
+    for (int g = 0; g < 4; ++g) stage(Flag<false>{}, min(g, n_groups - 1), g);
     wait_vmcnt<0>();
     lds_barrier();
     if (wave < NA) compute_E(0, 0, false);   // the spare wavefront has no alpha slot
@@ -482,14 +513,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // computes: wavefronts 0-3 those of E(jg+1) (in Stg[(jg+1) % 4]) for the E half that follows,
     // wavefronts 4-7 those of E(jg+2) (in Stg[(jg+2) % 4]) for the start of the next step, so no
     // E half begins with an LDS wait.
-    // Every wavefront issues stage(jg + 4) [2 transfers] inside its matrix-core half, which also
+    // Every wavefront issues stage(jg + 4) [NT transfers] inside its matrix-core half, which also
     // issues C*RBW X loads (the last chunk of group jg, then the other chunks of group jg + 1), XS
     // of them before the staging.  A staged buffer is filled by the transfers of all wavefronts, so
     // each wavefront waits for its own share of stage(jg + 3), issued in step jg - 1, right before
     // the barrier that ends step jg; it is read from step jg + 1 on (wavefronts 4-7 read the first
     // inputs of E(jg + 3) at the end of step jg + 1).  Vector-memory operations complete in issue
     // order, and after that staging a wavefront has issued the rest of that half (C*RBW - XS loads)
-    // and one more matrix-core half (C*RBW + 2 operations).  The compiler's own waits for the X
+    // and one more matrix-core half (C*RBW + NT operations).  The compiler's own waits for the X
     // registers, which cannot see the staging transfers, wait at most for a staging issued one E
     // half earlier.  The prologue waited for stages 0-3.
     const bool mfma_first = (wave & 4) == 0;
@@ -502,14 +533,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int sjg = min(jg + 4, n_groups - 1);
         const bool next = jg + 1 < n_groups;   // the last step has no E tile to prepare
         if (mfma_first) {
-            mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn);
+            mfma_group(Flag<true>{}, Flag<C == 4>{}, jg, buf, sjg, sb, sbn);
             if (next) compute_E(sbn, buf ^ 1, true);
         } else {
             // the spare wavefront (no alpha slot of its own) skips the E half
             if (wave < NA && next) compute_E(sbn, buf ^ 1, true);
-            mfma_group(Flag<true>{}, jg, buf, sjg, sb, sbn2);
+            mfma_group(Flag<true>{}, Flag<false>{}, jg, buf, sjg, sb, sbn2);
         }
-        wait_vmcnt<2 * C * RBW - XS + 2>();
+        wait_vmcnt<2 * C * RBW - XS + NT>();
         lds_barrier();
     }
     // drain the trailing (redundant) transfers before the LDS is reused or released
@@ -640,7 +671,7 @@ namespace {
 // tiles costs more than that.
 constexpr int kNA = 7, kNW = 8;
 
-typedef void (*search_fn)(const u32x4*, int, int, const floatx4*, int, const float*, const float*, const float*,
+typedef void (*search_fn)(const u32x4*, int, int, const u32x4*, int, const float*, const float*, const float*,
                           uint32_t, int, int, int, int, double*);
 
 template <int RBW, bool CLIP>
@@ -689,7 +720,7 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
     size_t off = 0;
     p.off_s = off;    off = align256(off + (size_t)n_grid * K * sizeof(float));
     p.off_inv = off;  off = align256(off + (size_t)n_grid * K * sizeof(float));
-    p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(float));
+    p.off_wt = off;   off = align256(off + (size_t)p.nb * 16 * K * sizeof(uint16_t));
     p.off_xt = off;   off = align256(off + (size_t)xt_rows * K * sizeof(uint16_t));
     p.off_part = off; off = align256(off + (size_t)max_tb * p.nb * n_grid * sizeof(double));
     p.off_clip = off; off = align256(off + (size_t)n_grid * sizeof(float));
@@ -702,7 +733,7 @@ namespace {
 // W [K, N] into the tiled float32 stream at column block nb0 (its padding columns are zero).
 hipError_t tile_w(const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p, void* ws, int64_t nb0,
                   hipStream_t st) {
-    floatx4* Wt = (floatx4*)((char*)ws + p.off_wt) + nb0 * (K / 32) * 128;
+    u32x4* Wt = (u32x4*)((char*)ws + p.off_wt) + nb0 * (K / 32) * 64;
     const int64_t total = ((N + 15) / 16) * (K / 32) * 64;
     const unsigned tgrid = (unsigned)((total + 255) / 256);
     if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
@@ -720,7 +751,7 @@ hipError_t run_search_tiled(const uint16_t* X, int64_t T, int64_t K, const Searc
     char* base = (char*)ws;
     float* s_tab = (float*)(base + p.off_s);
     float* inv_tab = (float*)(base + p.off_inv);
-    floatx4* Wt = (floatx4*)(base + p.off_wt);
+    u32x4* Wt = (u32x4*)(base + p.off_wt);
     u32x4* Xt = (u32x4*)(base + p.off_xt);
     double* part = (double*)(base + p.off_part);
     const float* clip_tab = (const float*)(base + p.off_clip);
