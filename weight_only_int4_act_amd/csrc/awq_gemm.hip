@@ -22,6 +22,33 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
     return r;
 }
 
+namespace {
+// float32 x4 to / from the device-coherent level: buffer operations with the agent-scope
+// cache-policy bit (sc1), so a partial written on one die is read back on another.
+constexpr int kCpolAgent = 16;
+constexpr int kCpolStream = 2;   // non-temporal: data read once
+__device__ __forceinline__ void store4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolAgent);
+}
+__device__ __forceinline__ floatx4 load4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolAgent));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+}  // namespace
+
+// Split-K partials: workgroup z of a tile writes its float32 sums to part[z][m][n] with agent-scope
+// stores (written through to the device-coherent level, not left in one die's L2), waits for them
+// and bumps the tile's arrival counter with one agent-scope atomic; the workgroup that arrives last
+// reads every partial of the tile with agent-scope loads, adds them in K-block order (so the
+// result does not depend on the arrival order), writes Y and sets the counter back to zero.
+// Offsets of rows beyond M and columns beyond N lie outside the partials' buffer resource, where
+// stores are dropped and loads read zero.
+#ifndef AWQ_GEMV_MAX_KSPLIT
+#define AWQ_GEMV_MAX_KSPLIT 16      // most K blocks (arrivals at one counter) of a split-K product
+#endif
+
 // ---------------------------------------------------------------- M > 1: matrix-core product
 // Code word (i, n) holds rows 8i + j (j < 8) of column n at bits 4j..4j+3.  One and-or turns
 // nibbles j and j + 4 of a word (shifted right by 4j) into the bf16 pair (128 + q_j, 128 + q_{j+4}),
@@ -94,14 +121,15 @@ __global__ __launch_bounds__(256) void k_prep_x(const uint16_t* __restrict__ X, 
 // rows, 2 for up to 32), splitting the workgroup's groups of K between them (wavefront w takes groups gb + w, gb + w + 4, ...); a fixed-order sum through
 // LDS joins them.  Lane (r16, q) owns the 4 adjacent columns n0 = 64*bx + 4*r16 .. n0 + 3 (one
 // 16-byte code load per code row) and uses column n0 + j as column r16 of its j-th 16-column
-// matrix-core tile; its accumulators hold rows 4q .. 4q+3 of each 16-row block.  With ksplit > 1
-// the workgroups along K write float32 partials, added in a fixed order by k_gemv_reduce.
+// matrix-core tile; its accumulators hold rows 4q .. 4q+3 of each 16-row block.  With several
+// workgroups along K (gridDim.z), the last of a tile to arrive adds their partials (see above).
 template <int G, int MB>
 __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ Xp, const float* __restrict__ Sg,
                                                    int64_t mpad, int64_t M, const uint32_t* __restrict__ codes,
                                                    const float* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
-                                                   uint16_t* __restrict__ Y, float* __restrict__ part) {
+                                                   uint16_t* __restrict__ Y, float* __restrict__ part,
+                                                   uint32_t* __restrict__ cnt) {
     constexpr int C = G / 32;
     __shared__ floatx4 red[3][MB][4][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -208,24 +236,70 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
             for (int j = 0; j < 4; ++j) red[wave - 1][mb][j][lane] = acc[mb][j];
     }
     __syncthreads();
-    if (wave > 0 || !nvalid) return;
+    if (wave > 0) return;
+    // wavefront 0: rows (R0 + mb) * 16 + 4q + i, columns n0 .. n0+3, as float32 x4 over the columns
+    floatx4 v[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        floatx4 v[4];
+        floatx4 t[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = ((acc[mb][j] + red[0][mb][j][lane]) + red[1][mb][j][lane]) + red[2][mb][j][lane];
+        for (int j = 0; j < 4; ++j) t[j] = ((acc[mb][j] + red[0][mb][j][lane]) + red[1][mb][j][lane]) + red[2][mb][j][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t m = (R0 + mb) * 16 + 4 * q + i;
-            if (m >= M) continue;
-            if (gridDim.z == 1) {
-                const uint32_t lo = pack_bf16x2(v[0][i], v[1][i]), hi = pack_bf16x2(v[2][i], v[3][i]);
-                *(uint2*)(Y + m * N + n0) = uint2{lo, hi};
-            } else {
-                *(floatx4*)(part + ((int64_t)blockIdx.z * M + m) * N + n0) = floatx4{v[0][i], v[1][i], v[2][i], v[3][i]};
-            }
-        }
+        for (int i = 0; i < 4; ++i) v[mb][i] = floatx4{t[0][i], t[1][i], t[2][i], t[3][i]};
     }
+    auto row = [&](int mb, int i) { return (R0 + mb) * 16 + 4 * q + i; };
+    auto write_y = [&](const floatx4 (&w)[MB][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (nvalid && row(mb, i) < M)
+                    *(uint2*)(Y + row(mb, i) * N + n0) = uint2{pack_bf16x2(w[mb][i][0], w[mb][i][1]),
+                                                                pack_bf16x2(w[mb][i][2], w[mb][i][3])};
+    };
+    const int nz = gridDim.z;
+    if (nz == 1) {
+        write_y(v);
+        return;
+    }
+    const uint32_t pbytes = (uint32_t)((int64_t)nz * M * N * 4);
+    const __amdgpu_buffer_rsrc_t pr = rsrc(part, pbytes);
+    auto poff = [&](int64_t z, int mb, int i) {
+        return (nvalid && row(mb, i) < M) ? (uint32_t)(((z * M + row(mb, i)) * N + n0) * 4) : pbytes;
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store4_agent(pr, poff(blockIdx.z, mb, i), v[mb][i]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this workgroup's partial has landed
+    const int tile = blockIdx.x + gridDim.x * blockIdx.y;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old != (uint32_t)(nz - 1)) return;
+    constexpr int ZB = 4 / MB;   // K blocks whose loads are in flight together
+    floatx4 tot[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[mb][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < nz; z0 += ZB) {
+        floatx4 pv[ZB][MB][4];
+#pragma unroll
+        for (int u = 0; u < ZB; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[u][mb][i] = load4_agent(pr, z0 + u < nz ? poff(z0 + u, mb, i) : pbytes);
+#pragma unroll
+        for (int u = 0; u < ZB; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[mb][i] += pv[u][mb][i];
+    }
+    write_y(tot);
+    if (lane == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Buffer resource over a byte range (accesses beyond it read zero) and a 16-byte-per-lane direct
@@ -259,18 +333,21 @@ __device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0
 // four (double buffered: the next group's transfers are in flight while the current group's
 // products run).  Each wavefront keeps the code words, steps and zeros of its next group in a
 // second register buffer.  Every barrier first waits for all of the wavefront's memory operations,
-// so the transfers of the buffer it publishes have landed.
+// so the transfers of the buffer it publishes have landed.  With several workgroups along K, every
+// wavefront writes its columns' partials and the workgroup arrives once (see above).
 template <int G>
 __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restrict__ Xp, const float* __restrict__ Sg,
                                                        int64_t mpad, int64_t M, const uint32_t* __restrict__ codes,
                                                        const float* __restrict__ scales,
                                                        const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
-                                                       uint16_t* __restrict__ Y, float* __restrict__ part) {
+                                                       uint16_t* __restrict__ Y, float* __restrict__ part,
+                                                       uint32_t* __restrict__ cnt) {
     constexpr int C = G / 32, MB = 4;
     constexpr int NE = MB * C * 64;              // 16-byte x' entries of a group (MB row blocks x C chunks)
     constexpr int PT = NE / 256;                 // entries per thread (C of them)
     __shared__ u32x4 xs[2][NE];
     __shared__ floatx4 ss[2][MB * 4];            // x' sums of the group's 64 rows
+    __shared__ uint32_t arrival;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, r16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * 256 + 64 * wave + 4 * r16;
@@ -381,23 +458,59 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
         full_barrier();                           // xs[0] filled, xs[1] no longer read
     }
 
-    if (!nvalid) return;
+    floatx4 v[MB][4];   // rows (R0 + mb) * 16 + 4q + i, columns n0 .. n0+3
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t m = (R0 + mb) * 16 + 4 * q + i;
-            if (m >= M) continue;
-            if (gridDim.z == 1) {
-                const uint32_t lo = pack_bf16x2(acc[mb][0][i], acc[mb][1][i]);
-                const uint32_t hi = pack_bf16x2(acc[mb][2][i], acc[mb][3][i]);
-                *(uint2*)(Y + m * N + n0) = uint2{lo, hi};
-            } else {
-                *(floatx4*)(part + ((int64_t)blockIdx.z * M + m) * N + n0) =
-                    floatx4{acc[mb][0][i], acc[mb][1][i], acc[mb][2][i], acc[mb][3][i]};
-            }
-        }
+        for (int i = 0; i < 4; ++i) v[mb][i] = floatx4{acc[mb][0][i], acc[mb][1][i], acc[mb][2][i], acc[mb][3][i]};
+    auto row = [&](int mb, int i) { return (R0 + mb) * 16 + 4 * q + i; };
+    auto write_y = [&](const floatx4 (&w)[MB][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (nvalid && row(mb, i) < M)
+                    *(uint2*)(Y + row(mb, i) * N + n0) = uint2{pack_bf16x2(w[mb][i][0], w[mb][i][1]),
+                                                                pack_bf16x2(w[mb][i][2], w[mb][i][3])};
+    };
+    const int nz = gridDim.z;
+    if (nz == 1) {
+        write_y(v);
+        return;
     }
+    const uint32_t pbytes = (uint32_t)((int64_t)nz * M * N * 4);
+    const __amdgpu_buffer_rsrc_t pr = rsrc(part, pbytes);
+    auto poff = [&](int64_t z, int mb, int i) {
+        return (nvalid && row(mb, i) < M) ? (uint32_t)(((z * M + row(mb, i)) * N + n0) * 4) : pbytes;
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store4_agent(pr, poff(blockIdx.z, mb, i), v[mb][i]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial has landed
+    __syncthreads();
+    const int tile = blockIdx.x + gridDim.x * blockIdx.y;
+    if (tid == 0) arrival = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != (uint32_t)(nz - 1)) return;
+    floatx4 tot[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[mb][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < nz; ++z) {
+        floatx4 pv[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[mb][i] = load4_agent(pr, poff(z, mb, i));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[mb][i] += pv[mb][i];
+    }
+    write_y(tot);
+    if (tid == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
@@ -417,25 +530,6 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 // arrives last reads every partial of the block with agent-scope loads, adds them in K-block
 // order (so the result does not depend on the arrival order), writes Y and sets the counter back
 // to zero.  No wavefront waits on another workgroup, and there are no floating-point atomics.
-#ifndef AWQ_GEMV_MAX_KSPLIT
-#define AWQ_GEMV_MAX_KSPLIT 16      // most K blocks (arrivals at one counter) of the M = 1 product
-#endif
-
-namespace {
-// float32 x4 to / from the device-coherent level: buffer operations with the agent-scope
-// cache-policy bit (sc1), so a partial written on one die is read back on another.
-constexpr int kCpolAgent = 16;
-constexpr int kCpolStream = 2;   // non-temporal: data read once
-__device__ __forceinline__ void store4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolAgent);
-}
-__device__ __forceinline__ floatx4 load4_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolAgent));
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-}  // namespace
 
 constexpr int kGemvCols = 256;   // columns per workgroup (64 lanes x 4)
 constexpr int kGemvWaves = 4;    // wavefronts per workgroup
@@ -591,51 +685,6 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     if (lane == 0) __hip_atomic_store(cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Y[n] = bf16(sum_b part[b][n]) in a fixed order.  A workgroup takes 32 columns; thread (c, l)
-// adds partials b = l, l + 8, ... of column c (all its loads in flight at once), and the 8 sums of
-// a column are added in lane order through LDS.  Wide enough to keep many loads in flight even for
-// a few thousand columns.
-__global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int nkb, int N,
-                                                     uint16_t* __restrict__ Y) {
-    __shared__ float sm[8][32];
-    const int c = threadIdx.x & 31, l = threadIdx.x >> 5;
-    const int n = blockIdx.x * 32 + c;
-    const int nn = n < N ? n : N - 1;
-    float t = 0.f;
-    for (int b0 = l; b0 < nkb; b0 += 8 * 8) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = b0 + 8 * j < nkb ? part[(int64_t)(b0 + 8 * j) * N + nn] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t += v[j];
-    }
-    sm[l][c] = t;
-    __syncthreads();
-    if (l == 0 && n < N) {
-        float u = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u += sm[i][c];
-        const __bf16 o = (__bf16)u;
-        Y[n] = __builtin_bit_cast(uint16_t, o);
-    }
-}
-
-// Y = bf16(sum_b part[b]) for the matrix-core path, where there are few partials (ksplit <= 8)
-// and many outputs: each thread adds the partials of 4 adjacent outputs in a fixed order (all its
-// loads issued before the sum) and writes 4 bf16 values.
-__global__ __launch_bounds__(256) void k_part_reduce4(const floatx4* __restrict__ part, int nkb, int64_t n4,
-                                                      uint2* __restrict__ Y) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;
-    floatx4 v[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) v[b] = b < nkb ? part[b * n4 + i] : floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx4 t = v[0];
-#pragma unroll
-    for (int b = 1; b < 8; ++b) t += v[b];
-    Y[i] = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
-}
-
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -647,31 +696,24 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
     u32x4* Xp = (u32x4*)(base + p.off_xp);
     float* Sg = (float*)(base + p.off_sg);
     float* part = (float*)(base + p.off_part);
+    uint32_t* cnt = (uint32_t*)(base + p.off_cnt);
     // row blocks along x (up to 2^31 - 1), 256-channel blocks along y (K <= 16.7M)
     k_prep_x<G><<<dim3((unsigned)(p.mpad / 16), (unsigned)((K + 255) / 256)), 256, 0, st>>>(X, M, K, s, p.mpad, Xp, Sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
     if (p.variant == 1)
-        k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+        k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
     else if (p.variant == 2)
-        k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
+        k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
     else
-        k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part);
-    e = hipGetLastError();
-    if (e != hipSuccess || p.ksplit == 1) return e;
-    if (p.ksplit <= 8) {
-        const int64_t n4 = M * N / 4;   // N % 8 == 0
-        k_part_reduce4<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((const floatx4*)part, p.ksplit, n4, (uint2*)Y);
-    } else {
-        k_gemv_reduce<<<(unsigned)((M * N + 31) / 32), 256, 0, st>>>(part, p.ksplit, (int)(M * N), Y);
-    }
+        k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
     return hipGetLastError();
 }
 }  // namespace
 
 // Every layout keeps the first kGemmCounterBytes of the workspace for the arrival counters of the
-// M <= 16 kernel and puts its data after them, so the counters (zero between calls) survive calls
+// split-K products and puts its data after them, so the counters (zero between calls) survive calls
 // of any shape that share one workspace.
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     GemmPlan p{};
@@ -714,14 +756,19 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     p.grid_x = p.variant == 5 ? (N + 255) / 256 : (N + 63) / 64;
     p.grid_y = p.mpad / rows;
     // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping enough
-    // groups per workgroup and the partials' index range within int
+    // groups per workgroup, at most AWQ_GEMV_MAX_KSPLIT arrivals per tile and the partials within the
+    // 32-bit byte range of a buffer resource (tiles < 512 whenever K is split, so the arrival
+    // counters of the tiles fit their region)
     const int64_t tiles = p.grid_x * p.grid_y;
     int64_t ks = 1;
     const int64_t min_groups = p.variant == 5 ? 2 : 4;   // two (one prefetched) or one per wavefront
-    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks * M * N < ((int64_t)1 << 31)) ks *= 2;
+    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks <= AWQ_GEMV_MAX_KSPLIT &&
+           2 * ks * M * N < ((int64_t)1 << 30))
+        ks *= 2;
     p.grid_z = ks;
     p.ksplit = (int)ks;
-    size_t off = kGemmCounterBytes;   // the counter region is never used for data (see plan_gemm's M <= 16 case)
+    p.off_cnt = 0;
+    size_t off = kGemmCounterBytes;   // the counter region is never used for data
     p.off_part = off; off = align256(off + (ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0));
     p.off_xp = off;   off = align256(off + (size_t)p.mpad * K * sizeof(uint16_t));
     p.off_sg = off;   off = align256(off + (size_t)n_groups * p.mpad * sizeof(float));
