@@ -250,8 +250,8 @@ int awq_greedy_search(const void* W_bf16, int64_t K, int64_t N, const float* mea
  *   X  bf16 [M, K];  s  float32 [K];  codes/scales/zeros as written by awq_pack;
  *   Y  bf16 [M, N] out.  Accumulation is float32; x/s is rounded to bf16 once.
  *   workspace >= awq_w4a16_gemm_workspace_size(M, K, N, group_size) bytes (the size may be 0),
- *   256-byte aligned.  Its first 64 KiB hold the arrival counters of the M = 1 product (one
- *   32-bit counter per 256 output columns): they must be ZERO before the first call that uses
+ *   256-byte aligned.  Its first 64 KiB hold the arrival counters of the split-K products (one
+ *   32-bit counter per output tile whose K range is split): they must be ZERO before the first call that uses
  *   the workspace (a zero-filled allocation), this function writes nothing else there and every
  *   completed call leaves them zero, so one workspace serves any sequence of calls of any shape
  *   without clearing (re-zero it after using the memory for anything else).  After them: M = 1
