@@ -538,7 +538,13 @@ constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 // split each group into G/VG slices (each with the group's step and zero, and the sum of x' over
 // its own rows in the offset/zero correction, which is linear in the rows), so that more
 // workgroups share K and fill the GPU.
-template <int G, int VG, int kGemvGpw>
+// QR: lanes per column quadruple.  QR = 1: lane l owns columns 4l .. 4l+3 of the workgroup's 256
+// and reads every code row of a slice.  QR = 4: the workgroup owns 64 columns; lane (r16, rq),
+// r16 = l % 16, rq = l / 16, owns columns 4 r16 .. 4 r16 + 3 and reads the code rows rq, rq + 4, ...
+// of a slice, and the four lanes of a column quadruple add their dot products with two lane swaps
+// at the end of the slice.  Narrow layers get four times as many workgroups without a longer K
+// split.
+template <int G, int VG, int kGemvGpw, int QR>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
                                                     const uint32_t* __restrict__ codes,
                                                     const float* __restrict__ scales,
@@ -546,7 +552,10 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ Y, float* __restrict__ part,
                                                     uint32_t* __restrict__ cnt) {
     static_assert(G % VG == 0 && VG >= 32, "slice of a group");
+    static_assert(QR == 1 || QR == 4, "lanes per column quadruple");
     constexpr int R = VG / 8;                    // code rows per slice
+    constexpr int RL = R / QR;                   // code rows per lane and slice
+    constexpr int COLS = kGemvCols / QR;         // columns per workgroup
     constexpr int NG = kGemvWaves * kGemvGpw;    // slices per workgroup
     // x' of the workgroup's slices: slot i, code row r, pair j: bf16 (x'_{8r+j}, x'_{8r+j+4})
     __shared__ uint32_t xpair[NG][VG / 2];
@@ -555,23 +564,24 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
     const int n_groups = K / VG;                 // slices, from here on called groups
-    const int n0 = cb * kGemvCols + lane * 4;
+    const int rq = QR == 1 ? 0 : lane / (64 / QR);   // this lane's first code row of a slice
+    const int n0 = cb * COLS + 4 * (lane % (64 / QR));
     const bool nvalid = n0 < N;                  // N % 4 == 0
     const int nc = nvalid ? n0 : N - 4;
     auto group_of = [&](int i) { return kb * NG + kGemvWaves * i + wave; };   // i-th group of this wave
 
     struct Buf {
-        u32x4 cw[R];
+        u32x4 cw[RL];
         floatx4 dsc;
         uint32_t zw;
     };
     Buf b0, b1;
     auto issue = [&](int i, Buf& b) {
         const int gg = min(group_of(i), n_groups - 1);
-        const uint32_t* cbase = codes + (int64_t)gg * R * N + nc;
+        const uint32_t* cbase = codes + ((int64_t)gg * R + rq) * N + nc;
 #pragma unroll
-        for (int r = 0; r < R; ++r)   // read once: streaming (non-temporal) loads
-            b.cw[r] = __builtin_nontemporal_load((const u32x4*)(cbase + (int64_t)r * N));
+        for (int r = 0; r < RL; ++r)   // read once: streaming (non-temporal) loads
+            b.cw[r] = __builtin_nontemporal_load((const u32x4*)(cbase + (int64_t)(QR * r) * N));
         const int qg = gg / (G / VG);            // the quantization group of the slice
         b.dsc = *(const floatx4*)(scales + (int64_t)qg * N + nc);
         b.zw = *(const uint32_t*)(zeros + (int64_t)qg * N + nc);
@@ -623,10 +633,10 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
         if (group_of(i) >= n_groups) return;
         float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RL; ++r) {
             uint32_t xp[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xp[j] = xpair[slot][4 * r + j];   // broadcast reads
+            for (int j = 0; j < 4; ++j) xp[j] = xpair[slot][4 * (QR * r + rq) + j];   // broadcast reads
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t w = b.cw[r][c];
@@ -636,6 +646,14 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                     d[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
                                                            __builtin_bit_cast(bf16x2_t, xp[j]), d[c], false);
                 }
+            }
+        }
+        if constexpr (QR == 4) {
+            // the four lanes of the column quadruple (l, l ^ 16, l ^ 32, l ^ 48)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                d[c] += __shfl_xor(d[c], 16, 64);
+                d[c] += __shfl_xor(d[c], 32, 64);
             }
         }
         const float sx = sxs[slot];
@@ -660,12 +678,14 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     if (wave > 0) return;
     // wavefront 0, lane l: columns n0 .. n0 + 3 of the block
     const floatx4 v = ((floatx4{acc[0], acc[1], acc[2], acc[3]} + red[0][lane]) + red[1][lane]) + red[2][lane];
+    const bool own = nvalid && rq == 0;          // the other lanes of a quadruple hold the same sums
     if (nkb == 1) {
-        if (nvalid) *(uint2*)(Y + n0) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (own) *(uint2*)(Y + n0) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         return;
     }
-    const __amdgpu_buffer_rsrc_t pr = rsrc(part, (uint32_t)((int64_t)nkb * N * 4));
-    if (nvalid) store4_agent(pr, (uint32_t)(((int64_t)kb * N + n0) * 4), v);
+    const uint32_t pbytes = (uint32_t)((int64_t)nkb * N * 4);
+    const __amdgpu_buffer_rsrc_t pr = rsrc(part, pbytes);
+    if (own) store4_agent(pr, (uint32_t)(((int64_t)kb * N + n0) * 4), v);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial has landed
     uint32_t old = 0;
     if (lane == 0) old = __hip_atomic_fetch_add(cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -677,11 +697,12 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     for (int b0 = 0; b0 < nkb; b0 += 16) {
         floatx4 p[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) p[u] = load4_agent(pr, (uint32_t)(((int64_t)(b0 + u) * N + n0) * 4));
+        for (int u = 0; u < 16; ++u)
+            p[u] = load4_agent(pr, rq == 0 ? (uint32_t)(((int64_t)(b0 + u) * N + n0) * 4) : pbytes);
 #pragma unroll
         for (int u = 0; u < 16; ++u) t += p[u];
     }
-    if (nvalid) *(uint2*)(Y + n0) = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+    if (own) *(uint2*)(Y + n0) = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
     if (lane == 0) __hip_atomic_store(cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -732,6 +753,15 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
         p.vgroup = (int)vg;
         p.gpw = (int)gpw;
         p.grid_y = (K / vg + kGemvWaves * gpw - 1) / (kGemvWaves * gpw);
+        // several slices per wavefront (long K): 64 columns per workgroup instead of 256, four times
+        // as many workgroups with the same K split (measured on K = 28672: 32-33 against 35-36 us;
+        // on layers with one slice per wavefront it was no faster), while the column blocks'
+        // counters fit their region
+        p.qr = 1;
+        if (gpw > 1 && (N + 63) / 64 <= (int64_t)(kGemmCounterBytes / sizeof(uint32_t))) {
+            p.qr = 4;
+            p.grid_x = (N + 63) / 64;
+        }
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
         p.mpad = 1;
@@ -781,10 +811,14 @@ template <int G, int VG>
 void launch_gemv(const uint16_t* X, const float* s, const uint32_t* codes, const float* scales, const uint8_t* zeros,
                  int64_t K, int64_t N, uint16_t* Y, float* part, uint32_t* cnt, const GemmPlan& p, hipStream_t st) {
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
-    if (p.gpw == 1)
-        k_w4a16_gemv<G, VG, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+    if (p.qr == 1 && p.gpw == 1)
+        k_w4a16_gemv<G, VG, 1, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+    else if (p.qr == 1)
+        k_w4a16_gemv<G, VG, 4, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+    else if (p.gpw == 1)
+        k_w4a16_gemv<G, VG, 1, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
     else
-        k_w4a16_gemv<G, VG, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+        k_w4a16_gemv<G, VG, 4, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
 }
 }  // namespace
 
