@@ -1,5 +1,5 @@
-"""The decode-shaped W4A16 product (M <= 16: one kernel per call, split-K partials summed by the
-last workgroup of each column block) against the fp64 oracle.
+"""The W4A16 product at decode-like sizes (split-K partials summed inside the product by the last
+workgroup of each output tile to arrive) against the fp64 oracle.
 
 One workspace serves a whole sequence of calls with changing activations and shapes, as a
 serving loop would use it: a partial left over from an earlier call, or an arrival counter not
@@ -31,6 +31,10 @@ SHAPES = [
     (1, 384, 40, 128, True),
     (16, 128, 8, 128, False),
     (9, 4096, 12296, 128, True),
+    # M = 1 with several slices per wavefront (64-column workgroups), ragged N, each group size
+    (1, 16384, 1032, 128, True),
+    (1, 12288, 520, 64, False),
+    (1, 10240, 264, 32, True),
 ]
 
 _packed = {}
