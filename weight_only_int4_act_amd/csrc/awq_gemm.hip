@@ -786,13 +786,14 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     p.grid_x = p.variant == 5 ? (N + 255) / 256 : (N + 63) / 64;
     p.grid_y = p.mpad / rows;
     // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping enough
-    // groups per workgroup, at most AWQ_GEMV_MAX_KSPLIT arrivals per tile and the partials within the
-    // 32-bit byte range of a buffer resource (tiles < 512 whenever K is split, so the arrival
-    // counters of the tiles fit their region)
+    // groups per workgroup, at most 8 K blocks per tile (the last arrival reads a partial of the
+    // whole row tile per K block; 8 measured 1-2 us faster than 16 on the narrow layers) and the
+    // partials within the 32-bit byte range of a buffer resource (tiles < 512 whenever K is split,
+    // so the arrival counters of the tiles fit their region)
     const int64_t tiles = p.grid_x * p.grid_y;
     int64_t ks = 1;
     const int64_t min_groups = p.variant == 5 ? 2 : 4;   // two (one prefetched) or one per wavefront
-    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks <= AWQ_GEMV_MAX_KSPLIT &&
+    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks <= 8 &&
            2 * ks * M * N < ((int64_t)1 << 30))
         ks *= 2;
     p.grid_z = ks;
