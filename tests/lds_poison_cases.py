@@ -1,0 +1,111 @@
+"""Parity cases run against the LDS-poison debug build of libawq (child process of
+tests/test_gpu_lds_poison.py; AWQ_LIBRARY names the library).
+
+In that build every pipelined LDS buffer (the search's E tiles and staging ring, the W4A16 products'
+staged x' and cross-wavefront sums) is filled with NaN between its last reader and its next writer,
+so a read that a missing wait or barrier lets run early yields NaN instead of stale but plausible
+data.  Each case is checked as the main parity tests check it: search losses within 1e-2 of the
+fp64 oracle ("AWQ (Activation-aware Weight Quantization)", 缩放因子优化的完整流程 steps 3-6), the
+chosen scale row, packed steps and zeros bit-exact and codes bit-exact outside near-ties, and the
+W4A16 product within 2e-2 (Frobenius) of the oracle's (推理时的等效实现).  Prints one line per case;
+exits non-zero on the first failure.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from oracle import awq_oracle as O  # noqa: E402
+from weight_only_int4_act_amd import inputs as I  # noqa: E402
+from tests.gpu_util import awq, gpu_gemm, gpu_layer, log, rel_fro  # noqa: E402
+
+
+def check_layer(L, g, zp, ng, label):
+    X64 = I.bf16_to_f64(L.X)
+    W64 = I.bf16_to_f64(L.W)
+    gpu = gpu_layer(L.X, L.W, g, zp, ng)
+    _, m = O.act_stats(X64)
+    assert np.array_equal(gpu["mean_abs"], m), label
+    S = O.scale_table(m, ng)
+    Lo = O.losses(X64, W64, S, g, zp)
+    assert np.all(np.isfinite(gpu["losses"])), (label, gpu["losses"])
+    rel = np.abs(gpu["losses"] - Lo) / np.maximum(Lo, 1e-300)
+    b = gpu["best"]
+    assert np.all(rel <= 1e-2), (label, rel.max())
+    assert Lo[b] <= 1.01 * Lo.min(), label
+    assert np.array_equal(gpu["s_best"], S[b]), label
+    w, d, z = O.pack(W64, S[b], g, zp)
+    P = S[b].astype(np.float64)[:, None] * W64
+    t, tz = O.pre_round_values(P, d, g, zp)
+    ties = O.near_tie(t) | np.repeat(O.near_tie(tz), g, axis=0)
+    bad = O.unpack_nibbles(w) != O.unpack_nibbles(gpu["codes"])
+    assert not np.any(bad & ~ties), (label, int((bad & ~ties).sum()))
+    assert np.array_equal(gpu["scales"], d) and np.array_equal(gpu["zeros"], z), label
+    log(f"[poison] search {label}: max rel loss err {rel.max():.2e}, best {b}, code mismatches {int(bad.sum())} "
+        f"(near-ties {int(ties.sum())}): ok")
+    return gpu
+
+
+def check_gemm(L, gpu, g, Ms, label):
+    for M in Ms:
+        Xm = L.X[:M].contiguous()
+        Y = gpu_gemm(Xm, gpu["q"])
+        assert np.all(np.isfinite(Y)), (label, M)
+        Yr = O.w4a16_ref(I.bf16_to_f64(Xm), gpu["s_best"], gpu["codes"], gpu["scales"], gpu["zeros"], g)
+        err = rel_fro(Y, Yr)
+        assert err <= 2e-2, (label, M, err)
+        log(f"[poison] gemm {label} M={M}: rel err {err:.2e}: ok")
+
+
+def check_packed_gemm(M, K, N, g, zp, seed):
+    """A W4A16 product on weights packed by the library at random scales (no search)."""
+    A = awq()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(seed)
+    W = torch.from_numpy((rng.standard_normal((K, N)) / np.sqrt(K)).astype(np.float32)).to(torch.bfloat16)
+    s = torch.from_numpy(np.exp(0.5 * rng.standard_normal(K)).astype(np.float32))
+    X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    cfg = A.qconfig(g, zp, 21)
+    codes = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float32, device=dev)
+    zeros = torch.empty((K // g, N), dtype=torch.uint8, device=dev)
+    A.awq_pack(W.to(dev), s.to(dev), cfg, codes, scales, zeros)
+    q = A.Quantized(codes, scales, zeros, s.to(dev), g)
+    Y = gpu_gemm(X, q)
+    assert np.all(np.isfinite(Y)), (M, K, N)
+    Yr = O.w4a16_ref(I.bf16_to_f64(X), s.numpy(), codes.cpu().numpy().view(np.uint32), scales.cpu().numpy(),
+                     zeros.cpu().numpy(), g)
+    err = rel_fro(Y, Yr)
+    assert err <= 2e-2, (M, K, N, g, err)
+    log(f"[poison] gemm M={M} K={K} N={N} g={g}: rel err {err:.2e}: ok")
+
+
+def main():
+    A = awq()
+    lib = os.path.basename(A.LIB_PATH)
+    log(f"[poison] library {lib}")
+    assert lib == "libawq_ldspoison.so", lib
+    cases = [
+        (I.small(700, 384, 48, seed=3), 128, True, 21, "T=700 K=384 N=48 g=128 asym"),
+        (I.small(333, 256, 40, seed=4, group_size=64, zero_point=False), 64, False, 21, "T=333 g=64 sym"),
+        (I.small(257, 128, 24, seed=5, group_size=32), 32, True, 21, "T=257 g=32 asym"),
+        (I.small(600, 256, 32, seed=6), 128, True, 33, "n_grid=33"),
+    ]
+    for L, g, zp, ng, label in cases:
+        gpu = check_layer(L, g, zp, ng, label)
+        T = L.X.shape[0]
+        check_gemm(L, gpu, g, [1, 7, 16, 37, min(T, 256)], label)
+    # split-K products: M = 1 on 256- and 64-column workgroups, M = 16 and M = 40 with K split
+    check_packed_gemm(1, 8192, 1032, 128, True, seed=11)
+    check_packed_gemm(1, 16384, 264, 128, True, seed=12)
+    check_packed_gemm(16, 8192, 520, 128, True, seed=13)
+    check_packed_gemm(40, 8192, 1032, 64, False, seed=14)
+    log("[poison] all cases ok")
+
+
+if __name__ == "__main__":
+    main()

@@ -40,6 +40,17 @@ def test_library_exports_every_declared_symbol(awq):
     assert set(_declared()) == set(awq.EXPORTED)
 
 
+def test_lds_poison_build_exports_the_same_symbols(awq):
+    # the debug build used by the race test (tests/test_gpu_lds_poison.py) is the same ABI
+    import ctypes
+    path = os.path.join(os.path.dirname(awq.LIB_PATH), "libawq_ldspoison.so")
+    assert os.path.exists(path), path
+    lib = ctypes.CDLL(path)
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} is declared in awq.h but not exported by the debug build"
+    assert os.path.basename(awq.LIB_PATH) == "libawq.so"   # the product path loads the product build
+
+
 def test_status_strings(awq):
     assert awq.awq_status_string(0) == "ok"
     for st in (-1, -2, -3, -4):

@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libawq.so")
+# AWQ_LIBRARY names another build of the same ABI to load instead (the LDS-poison debug build,
+# libawq_ldspoison.so, for the race test); the product path loads libawq.so
+LIB_PATH = os.environ.get("AWQ_LIBRARY") or os.path.join(_PKG, "libawq.so")
 
 AWQ_OK = 0
 AWQ_ERR_INVALID_ARG = -1

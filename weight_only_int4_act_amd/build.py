@@ -3,7 +3,10 @@
     python -m weight_only_int4_act_amd.build
 
 Objects go to weight_only_int4_act_amd/_build/, the library to
-weight_only_int4_act_amd/libawq.so.  Every call recompiles.
+weight_only_int4_act_amd/libawq.so.  A second library, libawq_ldspoison.so, is the same sources
+compiled with AWQ_LDS_POISON (pipelined LDS buffers filled with NaN between their last reader and
+their next writer): a debug build for the race test, never loaded by the product path.  Every call
+recompiles both.
 """
 from __future__ import annotations
 
@@ -17,6 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
+LIB_POISON = os.path.join(PKG, "libawq_ldspoison.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled: the compiler never emits v_pk_{add,mul,fma}_f32.
@@ -36,27 +40,34 @@ def hipcc() -> str:
     return p
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, extra, tag = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs_list = [(src, [], "") for src in SOURCES] + [(src, ["-DAWQ_LDS_POISON"], "_poison") for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(jobs_list)))) as ex:
+        objs = list(ex.map(_compile, jobs_list))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], LIB_POISON)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LIB_POISON}")
     return LIB
 
 

@@ -35,6 +35,21 @@ __device__ __forceinline__ int xcd_tile(int block, int tiles_per_xcd) {
     return (block % kNumXcd) * tiles_per_xcd + block / kNumXcd;
 }
 
+// Debug build (compiled with AWQ_LDS_POISON): every pipelined LDS buffer is filled with NaN
+// between its last reader and its next writer, so a read that a missing wait or barrier lets run
+// early sees NaN (which reaches the outputs) instead of plausible stale data.  Off in the library
+// the product uses.
+#ifdef AWQ_LDS_POISON
+constexpr bool kLdsPoison = true;
+#else
+constexpr bool kLdsPoison = false;
+#endif
+// 16 bytes of NaN in every float32 and bf16 lane
+__device__ __forceinline__ u32x4 lds_nan16() { return u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; }
+// wait until this wavefront's LDS writes (the poison) have landed, before a direct transfer into
+// the same addresses is issued
+__device__ __forceinline__ void lds_write_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -133,6 +133,15 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
     constexpr int C = G / 32;
     __shared__ floatx4 red[3][MB][4][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if constexpr (kLdsPoison) {   // debug build: the cross-wavefront sums start as NaN
+        if (wave > 0) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) red[wave - 1][mb][j][lane] = __builtin_bit_cast(floatx4, lds_nan16());
+        }
+        __syncthreads();
+    }
     const int q = lane >> 4, r16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * 64 + 4 * r16;
     const bool nvalid = n0 < N;                  // N % 8 == 0: n0 < N implies n0 + 3 < N
@@ -376,6 +385,12 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
     const uint32_t xs_lds = (uint32_t)(uintptr_t)&xs[0][0];
     const uint32_t ss_lds = (uint32_t)(uintptr_t)&ss[0][0];
     auto xdma = [&](int64_t g, int buf) {
+        if constexpr (kLdsPoison) {   // debug build: NaN where this buffer's transfers will land
+#pragma unroll
+            for (int i = 0; i < PT; ++i) xs[buf][256 * i + 64 * wave + lane] = lds_nan16();
+            if (wave == 0 && lane < MB * 4) ss[buf][lane] = __builtin_bit_cast(floatx4, lds_nan16());
+            lds_write_fence();
+        }
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
             const int e = tid + 256 * i;
@@ -563,6 +578,12 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     __shared__ floatx4 red[kGemvWaves - 1][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
+    if constexpr (kLdsPoison) {   // debug build: x', its sums and the cross-wavefront sums start as NaN
+        for (int i = threadIdx.x; i < NG * (VG / 2); i += 256) (&xpair[0][0])[i] = 0x7fc07fc0u;
+        if (threadIdx.x < NG) sxs[threadIdx.x] = __builtin_nanf("");
+        if (wave > 0) red[wave - 1][lane] = __builtin_bit_cast(floatx4, lds_nan16());
+        __syncthreads();
+    }
     const int n_groups = K / VG;                 // slices, from here on called groups
     const int rq = QR == 1 ? 0 : lane / (64 / QR);   // this lane's first code row of a slice
     const int n0 = cb * COLS + 4 * (lane % (64 / QR));

@@ -494,6 +494,28 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         }
     };
 
+    // Debug build: NaN into this wavefront's share of a staging buffer (the entries its transfers
+    // fill) and into its E tile slot, at the start of the step in which they are refilled
+    auto poison_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < NT; ++r) Stg[buf][NW * 64 * r + wave * 64 + lane] = lds_nan16();
+    };
+    auto poison_E = [&](int ebuf) __attribute__((always_inline)) {
+        if (wave < NA) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) Es[ebuf][slot][c][lane] = lds_nan16();
+        }
+    };
+    if constexpr (kLdsPoison) {
+        if (lane == 0) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a) red[wave][a] = __builtin_nan("");
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) poison_stage(g);
+        lds_write_fence();
+    }
+
     // ---- prologue: the first X chunks in registers, inputs of groups 0-3 staged, E(0) computed.
 #pragma unroll
     for (int c = 0; c < (X3 ? 2 : XD); ++c) load_X(c / C, c % C, c);
@@ -532,6 +554,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
         const int sbn2 = (jg + 2) & 3;          // group jg + 2
         const int sjg = min(jg + 4, n_groups - 1);
         const bool next = jg + 1 < n_groups;   // the last step has no E tile to prepare
+        if constexpr (kLdsPoison) {
+            // Stg[sb] was last read by E(jg) in step jg - 1 and is refilled in this step; Es[buf ^ 1]
+            // was last read in step jg - 1 and receives E(jg + 1) in this step
+            poison_stage(sb);
+            poison_E(buf ^ 1);
+            lds_write_fence();
+        }
         if (mfma_first) {
             mfma_group(Flag<true>{}, Flag<C == 4>{}, jg, buf, sjg, sb, sbn);
             if (next) compute_E(sbn, buf ^ 1, true);
