@@ -106,7 +106,10 @@ def search_traffic():
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
         if search_source_digest() != rec["source_sha256"]:
             return None
-        return float(rec["bytes_per_launch"])
+        # bytes the L2s fetched from and wrote to the fabric per launch, each counter scaled by
+        # what it reads for a copy of known size
+        return float(rec["fetch_kib"]) * 1024 * float(rec["fetch_factor"]) + \
+            float(rec["write_kib"]) * 1024 * float(rec["write_factor"])
     except (OSError, IndexError, KeyError, ValueError):
         return None
 
