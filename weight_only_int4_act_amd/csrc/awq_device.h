@@ -44,8 +44,21 @@ constexpr bool kLdsPoison = true;
 #else
 constexpr bool kLdsPoison = false;
 #endif
-// 16 bytes of NaN in every float32 and bf16 lane
-__device__ __forceinline__ u32x4 lds_nan16() { return u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; }
+// 0x7ff87ff8: NaN as float32, as both bf16 halves and, in pairs, as float64
+constexpr uint32_t kLdsNan = 0x7ff87ff8u;
+__device__ __forceinline__ u32x4 lds_nan16() { return u32x4{kLdsNan, kLdsNan, kLdsNan, kLdsNan}; }
+// Debug build: fill a workgroup's floating-point LDS array with NaN at kernel start (every thread
+// strides over it), then a barrier; a no-op otherwise.  Called by every thread, before any early
+// return.
+template <typename T>
+__device__ __forceinline__ void lds_poison_start(T* p, int count) {
+    if constexpr (kLdsPoison) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        const int words = (int)(count * sizeof(T) / 4);
+        for (int i = (int)threadIdx.x; i < words; i += (int)blockDim.x) q[i] = kLdsNan;
+        __syncthreads();
+    }
+}
 // wait until this wavefront's LDS writes (the poison) have landed, before a direct transfer into
 // the same addresses is issued
 __device__ __forceinline__ void lds_write_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void k_prep_x(const uint16_t* __restrict__ X, 
                                                 const float* __restrict__ s, int64_t mpad, u32x4* __restrict__ Xp,
                                                 float* __restrict__ Sg) {
     __shared__ u32x4 tile[512];
+    lds_poison_start(&tile[0], 512);
     const int kbl = threadIdx.x & 31, ml = threadIdx.x >> 5;
     const int64_t kbs = K / 8, kchunks = K / 32;
     const int64_t kb = (int64_t)blockIdx.y * 32 + kbl;
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
     if constexpr (kLdsPoison) {   // debug build: x', its sums and the cross-wavefront sums start as NaN
-        for (int i = threadIdx.x; i < NG * (VG / 2); i += 256) (&xpair[0][0])[i] = 0x7fc07fc0u;
+        for (int i = threadIdx.x; i < NG * (VG / 2); i += 256) (&xpair[0][0])[i] = kLdsNan;
         if (threadIdx.x < NG) sxs[threadIdx.x] = __builtin_nanf("");
         if (wave > 0) red[wave - 1][lane] = __builtin_bit_cast(floatx4, lds_nan16());
         __syncthreads();

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(256) void k_greedy_step(const uint16_t* __restrict_
         float scale[G];            // s_j of the group's channels
         int idx[G];
     } sh;
+    lds_poison_start(&sh.ms[0], P * (CH + 1) + 8 * 32 + 32 + 4 * 32);   // ms, chunk, sum, wave
+    lds_poison_start(&sh.scale[0], G);
     double* const s_ms = sh.ms;
     double* const sm_chunk = sh.chunk;
     double* const sm_sum = sh.sum;
@@ -284,6 +286,8 @@ __global__ __launch_bounds__(256) void k_greedy_final(int32_t* __restrict__ idx,
                                                       double* __restrict__ err) {
     __shared__ double sm_chunk[8 * 32];
     __shared__ double sm_sum[32];
+    lds_poison_start(&sm_chunk[0], 8 * 32);
+    lds_poison_start(&sm_sum[0], 32);
     const int grp = blockIdx.x;
     const int64_t k0 = (int64_t)grp * G;
     const int one = n_cand / 2;

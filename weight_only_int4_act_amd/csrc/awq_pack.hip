@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                                               uint32_t* __restrict__ codes, float* __restrict__ scales,
                                               uint8_t* __restrict__ zeros) {
     __shared__ float sg[G];   // the group's scales, shared by the workgroup's columns
+    lds_poison_start(&sg[0], G);
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t jg = blockIdx.y;
     const int64_t k0 = jg * G;

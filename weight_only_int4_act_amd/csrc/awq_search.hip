@@ -604,6 +604,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
 __global__ __launch_bounds__(256) void k_reduce_losses(const double* __restrict__ partials, int64_t tiles,
                                                        int n_grid, double* __restrict__ losses) {
     __shared__ double sm[256];
+    lds_poison_start(&sm[0], 256);
     const int i = blockIdx.x;
     double s = 0.0;
     for (int64_t t0 = threadIdx.x; t0 < tiles; t0 += 8 * 256) {   // 8 loads in flight, fixed order
@@ -628,6 +629,7 @@ __global__ __launch_bounds__(256) void k_reduce_losses_range(const double* __res
                                                              int64_t nb_total, int64_t nb0, int64_t nb1, int n_grid,
                                                              double* __restrict__ losses) {
     __shared__ double sm[256];
+    lds_poison_start(&sm[0], 256);
     const int i = blockIdx.x;
     const int64_t w = nb1 - nb0, tiles = tb * w;
     double s = 0.0;

@@ -23,6 +23,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(const uint16_t*
                                                                  int64_t K, int64_t rows_per_chunk,
                                                                  double* __restrict__ partial) {
     __shared__ double red[4][kStatsCols];
+    lds_poison_start(&red[0][0], 4 * kStatsCols);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t c0 = (int64_t)blockIdx.x * kStatsCols + lane * 8;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ 
                                                      double* __restrict__ sum_abs, int accumulate,
                                                      int64_t total_tokens, float* __restrict__ mean_abs) {
     __shared__ double sm[8][32];
+    lds_poison_start(&sm[0][0], 8 * 32);
     const int c = threadIdx.x & 31, l = threadIdx.x >> 5;
     const int64_t k = (int64_t)blockIdx.x * 32 + c;
     const int64_t kk = k < K ? k : K - 1;
@@ -163,6 +165,7 @@ hipError_t launch_scale_table(const float* mean_abs, int64_t K, int n_grid, floa
 __global__ __launch_bounds__(kStatsThreads) void k_max_partial(const uint16_t* __restrict__ X, int64_t T, int64_t K,
                                                               int64_t rows_per_chunk, float* __restrict__ partial) {
     __shared__ float red[4][kStatsCols];
+    lds_poison_start(&red[0][0], 4 * kStatsCols);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t c0 = (int64_t)blockIdx.x * kStatsCols + lane * 8;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
@@ -219,6 +222,7 @@ hipError_t launch_act_max(const uint16_t* X, int64_t T, int64_t K, float* max_ab
 __global__ __launch_bounds__(256) void k_weight_mean_abs(const uint16_t* __restrict__ W, int64_t K, int64_t N,
                                                          float* __restrict__ w_mean) {
     __shared__ double red[256];
+    lds_poison_start(&red[0], 256);
     const int64_t k = blockIdx.x;
     double s = 0.0;
     for (int64_t n = threadIdx.x; n < N; n += 256) s += (double)fabsf(bf16_lo((uint32_t)W[k * N + n]));
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(256) void k_scale_table_ex(const float* __restrict_
                                                         const float* __restrict__ w_mean, int64_t K, int n_grid,
                                                         int normalize, float* __restrict__ s_tab) {
     __shared__ double red[256];
+    lds_poison_start(&red[0], 256);
     const int i = blockIdx.x;
     const double a = (double)i / (double)(n_grid - 1);
     auto t_of = [&](int64_t k) {
