@@ -197,6 +197,56 @@ def near_tie(t: np.ndarray, rel: float = 1e-5) -> np.ndarray:
     return f <= rel * np.maximum(1.0, np.abs(t))
 
 
+def loss_tie_variants(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
+                      clip: float = 1.0, rel: float = 1e-5, max_ties: int = 12) -> np.ndarray:
+    """L = ||X (S^-1 Q'(S W) - W)||^2 for every admissible rounding Q' of the near-tie elements.
+
+    An element whose pre-round value p/Delta lies within ``rel`` of a .5 boundary (``near_tie``)
+    may take either neighbouring level, floor(p/Delta) or floor(p/Delta) + 1: both are correct
+    roundings up to the precision in which p/Delta is evaluated ([P3] section 4 rounds to the
+    nearest level; at a tie either neighbour is equally near).  Every other element keeps the
+    quantizer's level, and the step and zero of each group are the quantizer's.  A tie level is
+    taken as is, beyond the code range by one step at a tied range end, unless the range is
+    clipped (c < 1), where levels clamp to the clipped range as in ``quantize_groups``.
+
+    Returns the 2**n losses of the n near-tie elements' choices (n <= max_ties), the first with
+    every tie rounded as ``quantize_groups`` rounds it, i.e. ``loss(...)``.  Used only by the
+    parity tests, to accept a search loss that took a tie the other way.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    s64 = np.asarray(s, dtype=np.float64)
+    g = int(group_size)
+    P = s64[:, None] * W
+    codes, delta, zero = quantize_groups(P, g, zero_point, clip)
+    d = np.repeat(delta.astype(np.float64), g, axis=0)
+    z = np.repeat(zero.astype(np.float64), g, axis=0)
+    level = codes.astype(np.float64) - z            # the quantizer's level of every element
+    t, _ = pre_round_values(P, delta, g, zero_point, clip)
+    tie = np.argwhere(near_tie(t, rel))
+    n = len(tie)
+    if n > max_ties:
+        raise ValueError(f"{n} near-tie elements: more than max_ties={max_ties}")
+    lo_hi = None
+    if float(np.float32(clip)) < 1.0:
+        lo_hi = (-z, 15.0 - z) if zero_point else (np.full_like(z, -7.0), np.full_like(z, 7.0))
+    out = []
+    for mask in range(2 ** n):
+        lv = level.copy()
+        for b, (k, c) in enumerate(tie):
+            lf = np.floor(t[k, c])
+            other = lf + 1.0 if lv[k, c] == lf else lf
+            if (mask >> b) & 1:
+                v = other
+                if lo_hi is not None:
+                    v = min(max(v, lo_hi[0][k, c]), lo_hi[1][k, c])
+                lv[k, c] = v
+        E = lv * d / s64[:, None] - W
+        Y = X @ E
+        out.append(float(np.sum(Y * Y)))
+    return np.array(out)
+
+
 def dequantize(codes: np.ndarray, delta: np.ndarray, zero: np.ndarray, group_size: int) -> np.ndarray:
     """(code - zero) * Delta, broadcast per group along K -- float64 [K, N]."""
     g = int(group_size)

@@ -342,9 +342,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_search(
     // E tile of the group staged in Stg[ibuf], for alpha slot `slot`, into Es[ebuf][slot].  The
     // level is rint(p/Delta) without the clamp to the code range: with Delta and the zero taken
     // from the group's own max and min, the level leaves the range only when p/Delta lies at a .5
-    // tie at one end of the range, where either neighbour has the same |error| = Delta/2.  The loss
-    // is therefore unaffected up to the float32 rounding the search makes anyway; the packing
-    // kernel applies the quantizer exactly, clamp included.
+    // tie at one end of the range, where either neighbour is an equally near rounding (error
+    // +-Delta/2).  Like every tie the float32 evaluation meets, it may be taken the other way than
+    // the exact quantizer takes it: the sign of that element's error then differs, which moves the
+    // loss through its cross terms (percents on a layer of a few outputs, nothing measurable on
+    // real ones).  The packing kernel applies the quantizer exactly, clamp included.
     // The staged inputs are read two chunks ahead of their use, so that LDS latency overlaps the
     // arithmetic of the previous chunk.  The scale and reciprocal values of a chunk depend only on
     // the row, and the 16 lanes of a quad (one 16-lane DPP row) need the same 8 rows: lane 16q + j
