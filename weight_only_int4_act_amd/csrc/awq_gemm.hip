@@ -48,6 +48,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 #ifndef AWQ_GEMV_MAX_KSPLIT
 #define AWQ_GEMV_MAX_KSPLIT 16      // most K blocks (arrivals at one counter) of a split-K product
 #endif
+// 2..32 rows: the K split stops at about this many workgroups (one per CU)
+constexpr int64_t kGemmSkinnyWorkgroups = 256;
 
 // ---------------------------------------------------------------- M > 1: matrix-core product
 // Code word (i, n) holds rows 8i + j (j < 8) of column n at bits 4j..4j+3.  One and-or turns
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                                                    uint32_t* __restrict__ cnt) {
     constexpr int C = G / 32;
     __shared__ floatx4 red[3][MB][4][64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wavefront index in a scalar register: the group loop is then uniform per wavefront
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
     if constexpr (kLdsPoison) {   // debug build: the cross-wavefront sums start as NaN
         if (wave > 0) {
 #pragma unroll
@@ -164,32 +167,32 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // The code words, steps, zeros and x' sums of this wavefront's next group (and, for MB = 1, its
-    // x' fragments) are loaded before the current group's products are issued (two register
-    // buffers), so a group's memory reads are in flight during the previous group's matrix work.
-    constexpr bool XB = MB == 1;
+    // The code words, steps, zeros and x' sums of the wavefront's next group, and its x' fragments,
+    // are loaded before the current group's products are issued (two register buffers of each).  No
+    // load is issued under a condition (a load past the wavefront's last group reads that group
+    // again: a valid address, still in the cache) and scheduling barriers keep the next group's loads
+    // ahead of the current group's products, so the compiler counts the loads in flight exactly and
+    // each group waits for its own buffer only, not for the prefetch.
     struct Buf {
         u32x4 cw[C];
         floatx4 dsc;
         uint32_t zw;
         floatx4 sv[MB];
-        u32x4 a[XB ? C : 1][MB];
     };
-    auto issue = [&](int64_t g, Buf& b) {
+    auto issue = [&](int64_t g, Buf& b, u32x4 (&a)[C][MB]) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) b.cw[c] = *(const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc);
+        for (int c = 0; c < C; ++c)   // read once: streaming (non-temporal) loads
+            b.cw[c] = __builtin_nontemporal_load((const u32x4*)(codes + (g * (G / 8) + 4 * c + q) * N + nc));
         b.dsc = *(const floatx4*)(scales + g * N + nc);
         b.zw = *(const uint32_t*)(zeros + g * N + nc);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) b.sv[mb] = *(const floatx4*)(Sg + g * mpad + (R0 + mb) * 16 + 4 * q);
-        if constexpr (XB) {
 #pragma unroll
-            for (int c = 0; c < C; ++c)
+        for (int c = 0; c < C; ++c)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) b.a[c][mb] = Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
-        }
+            for (int mb = 0; mb < MB; ++mb) a[c][mb] = Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
     };
-    auto consume = [&](int64_t g, const Buf& b) {
+    auto consume = [&](const Buf& b, const u32x4 (&a)[C][MB]) {
         floatx4 accg[MB][4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -201,10 +204,6 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
             }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            u32x4 a[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                a[mb] = XB ? b.a[XB ? c : 0][mb] : Xp[((R0 + mb) * kchunks + g * C + c) * 64 + lane];
             const u32x4 cw = b.cw[c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                                        ((cw[j] >> 8) & nib) | bf128, ((cw[j] >> 12) & nib) | bf128};
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, bo),
+                    accg[mb][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[c][mb]), __builtin_bit_cast(bf16x8, bo),
                                                accg[mb][j]);
             }
         }
@@ -226,17 +225,25 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                 for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(b.dsc[j], accg[mb][j][i], acc[mb][j][i]);
     };
     {
-        // two groups per step, so each buffer keeps a fixed set of registers
         Buf b0, b1;
-        if (gb + wave < ge) issue(gb + wave, b0);
-        for (int64_t g = gb + wave; g < ge; g += 8) {
-            if (g + 4 < ge) issue(g + 4, b1);
-            consume(g, b0);
-            if (g + 4 < ge) {
-                if (g + 8 < ge) issue(g + 8, b0);
-                consume(g + 4, b1);
-            }
+        u32x4 a0[C][MB], a1[C][MB];
+        const int64_t nw = ge - gb > wave ? (ge - gb - wave + 3) / 4 : 0;   // the wavefront's groups
+        auto gw = [&](int64_t i) { return gb + wave + 4 * i; };            // its i-th group
+        const int64_t gl = nw > 0 ? gw(nw - 1) : n_groups - 1;
+        issue(min(gw(0), gl), b0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        int64_t i = 0;
+        for (; i + 2 <= nw; i += 2) {
+            issue(min(gw(i + 1), gl), b1, a1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(b0, a0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(min(gw(i + 2), gl), b0, a0);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(b1, a1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (i < nw) consume(b0, a0);
     }
 
     if (wave > 0) {
@@ -807,16 +814,20 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     p.variant = mb == 4 ? 5 : mb;
     p.grid_x = p.variant == 5 ? (N + 255) / 256 : (N + 63) / 64;
     p.grid_y = p.mpad / rows;
-    // split K across workgroups until ~512 workgroups are in flight (2 per CU), keeping enough
-    // groups per workgroup, at most 8 K blocks per tile (the last arrival reads a partial of the
-    // whole row tile per K block; 8 measured 1-2 us faster than 16 on the narrow layers) and the
-    // partials within the 32-bit byte range of a buffer resource (tiles < 512 whenever K is split,
-    // so the arrival counters of the tiles fit their region)
+    // split K across workgroups, keeping enough groups per workgroup, at most 8 K blocks per tile
+    // (the last arrival reads a partial of the whole row tile per K block; 8 measured 1-2 us faster
+    // than 16 on the narrow layers) and the partials within the 32-bit byte range of a buffer
+    // resource: 2..32 rows until about one workgroup per CU (fewer, longer workgroups: the partials'
+    // traffic and the arrival tail grow with the split; on the 70B-shaped block at M = 16, 256
+    // workgroups measured 2-3% faster than 512 or 768 and 13% faster than ~1000), more rows until
+    // ~512 workgroups are in flight (2 per CU).  Tiles < 512 whenever K is split, so the arrival
+    // counters of the tiles fit their region.
     const int64_t tiles = p.grid_x * p.grid_y;
     int64_t ks = 1;
-    const int64_t min_groups = p.variant == 5 ? 2 : 4;   // two (one prefetched) or one per wavefront
-    while (tiles * ks < 512 && 2 * ks * min_groups <= n_groups && 2 * ks <= 8 &&
-           2 * ks * M * N < ((int64_t)1 << 30))
+    const bool skinny = p.variant != 5;
+    const int64_t min_groups = skinny ? 4 : 2;   // one per wavefront and one prefetched, or two
+    auto wider = [&](int64_t k) { return skinny ? tiles * 2 * k <= kGemmSkinnyWorkgroups : tiles * k < 512; };
+    while (wider(ks) && 2 * ks * min_groups <= n_groups && 2 * ks <= 8 && 2 * ks * M * N < ((int64_t)1 << 30))
         ks *= 2;
     p.grid_z = ks;
     p.ksplit = (int)ks;
