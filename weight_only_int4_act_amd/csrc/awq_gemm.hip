@@ -340,7 +340,12 @@ __device__ __forceinline__ void gdma16(gi32x4 rsrc, uint32_t voff, uint32_t lds)
         : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "memory");
 }
-__device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// wait for every memory operation of the wavefront, then the workgroup barrier; written with the
+// builtins, so the compiler knows that no load is in flight after it
+__device__ __forceinline__ void full_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
 }  // namespace
 
 // M > 32: 64 rows (4 row blocks) x 256 columns per workgroup.  The 4 wavefronts walk the same K
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
     __shared__ u32x4 xs[2][NE];
     __shared__ floatx4 ss[2][MB * 4];            // x' sums of the group's 64 rows
     __shared__ uint32_t arrival;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int q = lane >> 4, r16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * 256 + 64 * wave + 4 * r16;
     const bool nvalid = n0 < N;                  // N % 8 == 0: n0 < N implies n0 + 3 < N
@@ -456,30 +461,29 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
                 for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(b.dsc[j], accg[mb][j][i], acc[mb][j][i]);
     };
     // one group per step: while the products of group g run (from xs[g & 1]), the loads of group
-    // g + 1 are in flight (x' into the other LDS buffer, codes into the other register buffer)
+    // g + 1 are in flight (x' into the other LDS buffer, codes into the other register buffer).
+    // The loads are issued unconditionally (past the K block's last group they read that group
+    // again, into the buffer no one reads any more) and held ahead of the products by scheduling
+    // barriers, so the compiler does not make the products wait for the prefetch.
     Buf b0, b1;
-    if (gb < ge) {
-        xdma(gb, 0);
-        issue(gb, b0);
-    }
+    const int64_t gl = max(ge - 1, (int64_t)0);   // (an empty K block reads its neighbour's last group, unused)
+    xdma(min(gb, gl), 0);
+    issue(min(gb, gl), b0);
     full_barrier();
-    for (int64_t g = gb; g < ge; g += 2) {
-        const bool n1 = g + 1 < ge;
-        if (n1) {
-            xdma(g + 1, 1);
-            issue(g + 1, b1);
-        }
+    int64_t g = gb;
+    for (; g + 2 <= ge; g += 2) {   // two groups per step, no branch between a prefetch and its use
+        xdma(min(g + 1, gl), 1);
+        issue(min(g + 1, gl), b1);
+        __builtin_amdgcn_sched_barrier(0);
         consume(b0, 0);
         full_barrier();                           // xs[1] filled, xs[0] no longer read
-        if (!n1) break;
-        const bool n2 = g + 2 < ge;
-        if (n2) {
-            xdma(g + 2, 0);
-            issue(g + 2, b0);
-        }
+        xdma(min(g + 2, gl), 0);
+        issue(min(g + 2, gl), b0);
+        __builtin_amdgcn_sched_barrier(0);
         consume(b1, 1);
         full_barrier();                           // xs[0] filled, xs[1] no longer read
     }
+    if (g < ge) consume(b0, 0);                   // the last of an odd number: already in place
 
     floatx4 v[MB][4];   // rows (R0 + mb) * 16 + 4q + i, columns n0 .. n0+3
 #pragma unroll
