@@ -823,9 +823,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
     // than 16 on the narrow layers) and the partials within the 32-bit byte range of a buffer
     // resource: 2..32 rows until about one workgroup per CU (fewer, longer workgroups: the partials'
     // traffic and the arrival tail grow with the split; on the 70B-shaped block at M = 16, 256
-    // workgroups measured 2-3% faster than 512 or 768 and 13% faster than ~1000), more rows until
-    // ~512 workgroups are in flight (2 per CU).  Tiles < 512 whenever K is split, so the arrival
-    // counters of the tiles fit their region.
+    // workgroups measured 2-3% faster than 512 or 768), more rows until ~512 workgroups are in
+    // flight (2 per CU).  Tiles < 512 whenever K is split, so the arrival counters of the tiles fit
+    // their region.
     const int64_t tiles = p.grid_x * p.grid_y;
     int64_t ks = 1;
     const bool skinny = p.variant != 5;
