@@ -35,6 +35,13 @@ SHAPES = [
     (1, 16384, 1032, 128, True),
     (1, 12288, 520, 64, False),
     (1, 10240, 264, 32, True),
+    # more than 32 rows with 33 groups split into 8 K blocks of 5: the last K block is empty (its
+    # workgroups prefetch a neighbour's group, never use it, and add zeros); likewise at g = 64
+    (64, 4224, 256, 128, True),
+    (48, 2112, 264, 64, False),
+    # 17..32 rows on 130 column tiles (K not split), 9 groups: wavefront 0 takes three (the odd
+    # one after the two-group steps), the others two
+    (24, 1152, 8320, 128, True),
 ]
 
 _packed = {}
