@@ -198,7 +198,7 @@ def near_tie(t: np.ndarray, rel: float = 1e-5) -> np.ndarray:
 
 
 def loss_tie_variants(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: int, zero_point: bool,
-                      clip: float = 1.0, rel: float = 1e-5, max_ties: int = 12) -> np.ndarray:
+                      clip: float = 1.0, rel: float = 1e-5, max_ties: int = 22) -> np.ndarray:
     """L = ||X (S^-1 Q'(S W) - W)||^2 for every admissible rounding Q' of the near-tie elements.
 
     An element whose pre-round value p/Delta lies within ``rel`` of a .5 boundary (``near_tie``)
@@ -209,9 +209,16 @@ def loss_tie_variants(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: i
     taken as is, beyond the code range by one step at a tied range end, unless the range is
     clipped (c < 1), where levels clamp to the clipped range as in ``quantize_groups``.
 
-    Returns the 2**n losses of the n near-tie elements' choices (n <= max_ties), the first with
-    every tie rounded as ``quantize_groups`` rounds it, i.e. ``loss(...)``.  Used only by the
-    parity tests, to accept a search loss that took a tie the other way.
+    The loss is a sum over output columns, ||X E||^2 = sum_n ||X e_n||^2, and an element's level
+    enters only its own column e_n, so the choices are enumerated column by column: each column
+    with ties contributes the change of its own loss under each of its 2**m roundings, and every
+    combination's loss is the base loss plus one change per column.
+
+    Returns the 2**n losses of the n near-tie elements' choices (n <= max_ties).  The first has
+    every tie rounded as ``quantize_groups`` rounds it and equals ``loss(...)``; within one column
+    the choices count in binary over that column's ties (the first tie the lowest bit), and the
+    columns' counts nest with the first tied column innermost.  Used only by the parity tests, to
+    accept a search loss that took a tie the other way.
     """
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -230,21 +237,31 @@ def loss_tie_variants(X: np.ndarray, W: np.ndarray, s: np.ndarray, group_size: i
     lo_hi = None
     if float(np.float32(clip)) < 1.0:
         lo_hi = (-z, 15.0 - z) if zero_point else (np.full_like(z, -7.0), np.full_like(z, 7.0))
-    out = []
-    for mask in range(2 ** n):
-        lv = level.copy()
-        for b, (k, c) in enumerate(tie):
-            lf = np.floor(t[k, c])
-            other = lf + 1.0 if lv[k, c] == lf else lf
-            if (mask >> b) & 1:
-                v = other
-                if lo_hi is not None:
-                    v = min(max(v, lo_hi[0][k, c]), lo_hi[1][k, c])
-                lv[k, c] = v
-        E = lv * d / s64[:, None] - W
-        Y = X @ E
-        out.append(float(np.sum(Y * Y)))
-    return np.array(out)
+    E0 = level * d / s64[:, None] - W
+    Y0 = X @ E0
+    total = np.array([float(np.sum(Y0 * Y0))])
+    cols = []
+    for k, c in tie:
+        if c not in cols:
+            cols.append(int(c))
+    for c in cols:
+        rows = [int(k) for k, cc in tie if cc == c]
+        y0 = X @ E0[:, c]                       # the column's base, by the variants' own route
+        base_c = float(np.dot(y0, y0))
+        change = []
+        for mask in range(2 ** len(rows)):
+            e = E0[:, c].copy()
+            for b, k in enumerate(rows):
+                if (mask >> b) & 1:
+                    lf = np.floor(t[k, c])
+                    v = lf + 1.0 if level[k, c] == lf else lf
+                    if lo_hi is not None:
+                        v = min(max(v, lo_hi[0][k, c]), lo_hi[1][k, c])
+                    e[k] = v * d[k, c] / s64[k] - W[k, c]
+            y = X @ e
+            change.append(float(np.dot(y, y)) - base_c)
+        total = (np.asarray(change)[:, None] + total[None, :]).reshape(-1)
+    return total
 
 
 def dequantize(codes: np.ndarray, delta: np.ndarray, zero: np.ndarray, group_size: int) -> np.ndarray:

@@ -9,6 +9,9 @@
   slices, the last with 5 alphas; n_grid 64: ten, the last with 1), against the oracle's losses
   over the same grid ("AWQ (Activation-aware Weight Quantization)", 缩放因子优化的完整流程 step 3
   with alpha_i = i / (n_grid - 1)).
+* Output widths that are not a multiple of 8 (the search and the packing take any N; rows of W
+  are then not 16-byte aligned, and the last 16-column block of the search is partly padding):
+  search losses, choice, steps, zeros and codes against the oracle.
 """
 import numpy as np
 import pytest
@@ -74,3 +77,10 @@ def test_long_alpha_grids(ng):
 def test_long_alpha_grid_symmetric():
     L = I.small(600, 192, 24, seed=40, group_size=64, zero_point=False)
     _check_layer(L.X, L.W, 64, False, 33, "n_grid=33 sym g=64")
+
+
+@pytest.mark.parametrize("T,K,N,g,zp", [(300, 256, 20, 128, True), (257, 384, 13, 64, False),
+                                        (200, 128, 70, 32, True)])
+def test_widths_not_a_multiple_of_8(T, K, N, g, zp):
+    L = I.small(T, K, N, seed=T + N, group_size=g, zero_point=zp)
+    _check_layer(L.X, L.W, g, zp, 21, f"T={T} K={K} N={N} g={g} zp={zp}")

@@ -1,7 +1,9 @@
 """Pins of oracle.loss_tie_variants: the search loss under every admissible rounding of near-tie
 elements ("AWQ 激活感知量化", section 4: round to the nearest level; at a .5 tie both neighbours
 are equally near).  Hand-computed cases with exact ties, a tied element at the end of the code
-range, a clipped range, and inputs without ties.
+range, a clipped range, ties in two columns, and inputs without ties; and, on a small layer with
+ties in several columns, the per-column enumeration against a brute-force recomputation of the
+whole loss for every choice.
 """
 import numpy as np
 
@@ -76,3 +78,64 @@ def test_scaled_tie_flips_the_sign_of_the_unscaled_error():
     X[0, 1] = 0.0
     X[0, 2] = 1.0
     assert O.loss_tie_variants(X, W, s, 8, False).tolist() == [0.0, 0.0]
+
+
+def test_ties_in_two_columns_combine_column_losses():
+    # column 0: ties at rows 1 and 2 as in the first case (column loss 1, 0, 0, 1); column 1
+    # (Delta = 1): p = 1.5 at row 3, a tie between 1 and 2 (error -+0.5, column loss 0.25 either
+    # way).  The token reads rows 1, 2 and 3.  First tied column innermost.
+    W = np.zeros((8, 2))
+    W[:, 0] = [7.0, 2.5, 0.5, 0, 0, 0, 0, 0]
+    W[:, 1] = [7.0, 0, 0, 1.5, 0, 0, 0, 0]
+    X = np.zeros((1, 8))
+    X[0, 1] = X[0, 2] = X[0, 3] = 1.0
+    V = O.loss_tie_variants(X, W, np.ones(8), 8, False)
+    assert V.tolist() == [1.25, 0.25, 0.25, 1.25, 1.25, 0.25, 0.25, 1.25]
+    assert V[0] == O.loss(X, W, np.ones(8), 8, False)
+
+
+def test_per_column_enumeration_matches_brute_force():
+    # integer weights with Delta = 1 (max |p| = 7 in every group) and ten half-integers, exact
+    # ties, spread over the columns; every choice recomputed as the whole layer's loss
+    rng = np.random.default_rng(11)
+    K, N, g = 16, 4, 8
+    W = rng.integers(-6, 7, size=(K, N)).astype(np.float64)
+    W[0::g, :] = 7.0
+    rows = [1, 2, 3, 5, 9, 10, 12, 6, 14, 11]
+    cols = [0, 0, 1, 1, 2, 2, 3, 3, 0, 1]
+    for k, c in zip(rows, cols):
+        W[k, c] += 0.5
+    X = rng.standard_normal((5, K))
+    s = np.ones(K)
+    V = O.loss_tie_variants(X, W, s, g, False)
+    codes, delta, zero = O.quantize_groups(W, g, False)
+    t, _ = O.pre_round_values(W, delta, g, False)
+    tie = np.argwhere(O.near_tie(t))
+    assert len(tie) == 10 and len(set(tie[:, 1].tolist())) == 4
+    d = np.repeat(delta.astype(np.float64), g, axis=0)
+    level = codes.astype(np.float64) - np.repeat(zero.astype(np.float64), g, axis=0)
+    brute = []
+    for mask in range(2 ** len(tie)):
+        lv = level.copy()
+        for b, (k, c) in enumerate(tie):
+            if (mask >> b) & 1:
+                lv[k, c] = 2.0 * np.floor(t[k, c]) + 1.0 - lv[k, c]   # the other neighbour
+        Y = X @ (lv * d - W)
+        brute.append(float(np.sum(Y * Y)))
+    assert len(V) == len(brute)
+    assert np.allclose(np.sort(V), np.sort(brute), rtol=1e-12, atol=0.0)
+    assert V[0] == O.loss(X, W, s, g, False)
+
+
+def test_scaled_tie_with_a_cross_term():
+    # as above (s = 2 on row 1, p = 1.5 a tie: error +0.25 or -0.25 in W units) plus row 2 with
+    # p = w = 0.25 (level 0, error -0.25); the token reads row 1 four times and row 2 once:
+    # X E = 4 (+-0.25) - 0.25, so L = 0.5625 for the quantizer's rounding and 1.5625 for the other
+    W = np.zeros((8, 1))
+    W[:, 0] = [7.0, 0.75, 0.25, 0, 0, 0, 0, 0]
+    s = np.ones(8)
+    s[1] = 2.0
+    X = np.zeros((1, 8))
+    X[0, 1] = 4.0
+    X[0, 2] = 1.0
+    assert O.loss_tie_variants(X, W, s, 8, False).tolist() == [0.5625, 1.5625]

@@ -56,24 +56,55 @@ __device__ __forceinline__ int kmap(int c, int q) {
 // W [K, N] bf16 -> Wt (bf16, matrix-core B order): for column block nb (16 columns), chunk kc (32
 // channels) and lane l, the 8 values W[G*(kc/C) + kmap(kc%C, l/16) + e][16*nb + l%16], e < 8, as one
 // 16-byte word (value e in the low half of 32-bit word e/2 when e is even, in the high half when
-// odd), so that a lane reads its 8 values of a chunk as one linear 16-byte word.  Columns beyond N
-// are zero (a zero column quantizes to zero error).
+// odd), stored at Wt[(nb*kchunks + kc)*64 + l], so that a lane reads its 8 values of a chunk as one
+// linear 16-byte word.  Columns beyond N are zero (a zero column quantizes to zero error).
+// A workgroup takes one group of rows (G) and 64 columns (4 column blocks): it reads the tile with
+// 16-byte loads along the rows (each row's 64 columns are one 128-byte line; 2-byte loads with
+// bounds checks where the tile reaches past N or the rows are not 16-byte aligned), transposes it
+// through LDS (column-major, rows padded so that 8 consecutive rows of a column are one aligned
+// 16-byte read) and writes each column block's C KB of the group as contiguous 16-byte stores.
 template <int G>
 __global__ __launch_bounds__(256) void k_tile_w(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                                int64_t total, u32x4* __restrict__ Wt) {
+                                                int vec, u32x4* __restrict__ Wt) {
     constexpr int C = G / 32;
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one (nb, kc, lane)
-    if (e >= total) return;
-    const int lane = (int)(e & 63);
-    const int64_t rest = e >> 6;
-    const int64_t kchunks = K / 32;
-    const int64_t kc = rest % kchunks, nb = rest / kchunks;
-    const int64_t k0 = (kc / C) * G + kmap<G>((int)(kc % C), lane >> 4);
-    const int64_t n = nb * 16 + (lane & 15);
-    uint32_t v[8];
+    constexpr int LD = G + 8;                    // LDS row pitch of a column, in bf16
+    __shared__ __align__(16) uint16_t t[64 * LD];
+    lds_poison_start(&t[0], 64 * LD);
+    const int64_t n_groups = K / G, kchunks = K / 32, nblocks = (N + 15) / 16;
+    const int64_t j = (int64_t)blockIdx.x % n_groups;     // group (fastest: a column block's
+    const int64_t c0 = (int64_t)blockIdx.x / n_groups * 64;   // output is written in order)
+    const int tid = threadIdx.x;
+    const bool full = vec && c0 + 64 <= N;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = n < N ? (uint32_t)W[(k0 + i) * N + n] : 0u;
-    Wt[e] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    for (int pass = 0; pass < C; ++pass) {
+        const int r = pass * 32 + tid / 8, cs = 8 * (tid % 8);
+        const uint16_t* src = W + (j * G + r) * N + c0 + cs;
+        uint16_t v[8];
+        if (full) {
+            const u32x4 w = *(const u32x4*)src;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = (uint16_t)(w[e] & 0xffffu);
+                v[2 * e + 1] = (uint16_t)(w[e] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = c0 + cs + e < N ? src[e] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[(cs + e) * LD + r] = v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int idx = tid + 256 * i;           // (column block cb, chunk c, lane), lane fastest
+        const int lane = idx & 63, c = (idx >> 6) % C, cb = (idx >> 6) / C;
+        const int64_t nb = c0 / 16 + cb;
+        if (nb >= nblocks) continue;
+        const int col = cb * 16 + (lane & 15);
+        const u32x4 w = *(const u32x4*)&t[col * LD + kmap<G>(c, lane >> 4)];
+        Wt[(nb * kchunks + j * C + c) * 64 + lane] = w;
+    }
 }
 
 // X [T, K] bf16 -> Xt: for 16-row block R, chunk kc and lane l, the 16 bytes lane l feeds to the
@@ -763,15 +794,16 @@ SearchPlan plan_search(int64_t T, int64_t K, int64_t N, int group_size, int zero
 
 namespace {
 
-// W [K, N] into the tiled float32 stream at column block nb0 (its padding columns are zero).
+// W [K, N] into the tiled bf16 stream at column block nb0 (its padding columns are zero).
 hipError_t tile_w(const uint16_t* W, int64_t K, int64_t N, const SearchPlan& p, void* ws, int64_t nb0,
                   hipStream_t st) {
     u32x4* Wt = (u32x4*)((char*)ws + p.off_wt) + nb0 * (K / 32) * 64;
-    const int64_t total = ((N + 15) / 16) * (K / 32) * 64;
-    const unsigned tgrid = (unsigned)((total + 255) / 256);
-    if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
-    else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
-    else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, total, Wt);
+    const unsigned tgrid = (unsigned)((N + 63) / 64 * (K / p.group_size));
+    // 16-byte row loads need 16-byte aligned rows
+    const int vec = N % 8 == 0 && ((uintptr_t)W & 15) == 0;
+    if (p.group_size == 32) k_tile_w<32><<<tgrid, 256, 0, st>>>(W, K, N, vec, Wt);
+    else if (p.group_size == 64) k_tile_w<64><<<tgrid, 256, 0, st>>>(W, K, N, vec, Wt);
+    else k_tile_w<128><<<tgrid, 256, 0, st>>>(W, K, N, vec, Wt);
     return hipGetLastError();
 }
 
