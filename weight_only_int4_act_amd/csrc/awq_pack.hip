@@ -9,11 +9,12 @@
 //
 // With a clip ratio c (the configuration's optional min-max clipping, "009. AWQ Integration",
 // 关键设计 5) both ends of the range are multiplied by c before the step and the zero are formed.
-// The quantizer is evaluated in float64.  p = s*w is exact there (a float32 times a bf16 has at
+// The quantizer is evaluated as in float64.  p = s*w is exact there (a float32 times a bf16 has at
 // most 32 significant bits), max/min are exact, the step and the zero come from single IEEE
 // divisions, and each code is the round-half-even of p/Delta exactly as a float64 division and
-// rint give it (rne_div), so codes, steps and zeros are reproducible bit for bit by any float64
-// evaluation of the same definition.
+// rint give it, so codes, steps and zeros are reproducible bit for bit by any float64 evaluation
+// of the same definition.  The codes take a float32 quotient wherever its rounding provably equals
+// that one, and the exact float64 rounding (rne_div) near a .5 boundary.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -88,6 +89,8 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
     }
     const double dd = (double)d;
     const double r = 1.0 / dd;
+    const float rf = 1.0f / d;
+    const float zf = (float)z;
     // recompute p in the second pass rather than keep G float64 values live from the first
     asm volatile("" ::: "memory");
 #pragma unroll
@@ -97,8 +100,17 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            double c = rne_div(pv(i + j), dd, r);
-            c = ZP ? fmin(fmax(c + z, 0.0), 15.0) : fmin(fmax(c, -7.0), 7.0) + 8.0;
+            // float32 first: q = fl(fl(s w) fl(1/Delta)) is within |q| 1.8e-7 of p/Delta (three
+            // roundings of 2^-24 each), so a q farther than |q| 4.8e-7 from a .5 boundary rounds
+            // to the same integer as p/Delta (q - rint(q) is exact).  A quotient that close to a
+            // boundary, or not finite (1/Delta overflows for a step below ~3e-39), takes the exact
+            // float64 rounding (rne_div), which settles ties to even as the definition does
+            const uint32_t h = wp[(i + j) / 2];
+            const float wv = ((i + j) & 1) ? bf16_hi(h) : bf16_lo(h);
+            const float q = (sg[i + j] * wv) * rf;
+            float c = rintf(q);
+            if (!(fabsf(fabsf(q - c) - 0.5f) > fabsf(q) * 4.8e-7f)) c = (float)rne_div(pv(i + j), dd, r);
+            c = ZP ? fminf(fmaxf(c + zf, 0.f), 15.f) : fminf(fmaxf(c, -7.f), 7.f) + 8.f;
             word |= (uint32_t)c << (4 * j);
         }
         codes[((k0 + i) >> 3) * N + n] = word;
