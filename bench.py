@@ -51,6 +51,7 @@ sys.path.insert(0, HERE)
 
 METRIC = "AWQ search TFLOP/s (% bf16 MFMA peak), 4096x4096 layer, 8192 calib tokens"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
+SPEC_MHZ = 2400                # the clock those peaks assume
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_VALU_TOPS = 39.32         # 256 CU x 4 SIMD x 16 lanes x 2.4 GHz: vector ops/s (fp32 unpacked = fp64 rate)
 GREEDY_OPS_PER_EVAL = 7        # multiply, round, clamp (2), fma, multiply, fma: one exact element error
@@ -72,6 +73,7 @@ def parse():
     ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-clock", action="store_true")
     ap.add_argument("--greedy-iters", type=int, default=3)
     ap.add_argument("--multi-iters", type=int, default=3)
     ap.add_argument("--gemv-iters", type=int, default=50)
@@ -249,6 +251,9 @@ def main():
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(search_ms, 4)},
         "best_alpha_index": int(best.item()),
     }
+    if not args.no_clock:
+        out["clock"] = observed_clock(lambda: A.awq_search(X, W, mean_abs, cfg, ws_search, losses, best, s_best,
+                                                           stream), torch, achieved)
 
     if not args.no_clip:
         out["clip_search"] = bench_clip(A, torch, dev, X, W, s_best, g, layer.zero_point, ws_search, stream,
@@ -432,6 +437,50 @@ def bench_multi(A, I, torch, dev, iters):
 
 def _gemv_bytes(K, N, g=128):
     return K * N // 2 + 4 * (K // g) * N + (K // g) * N + 4 * K + 2 * K + 2 * N
+
+
+def observed_clock(run_once, torch, achieved):
+    """The shader clock the chip holds under the search: the search runs back to back for ~1.5 s and
+    `amd-smi metric -c` is read once in the middle of it (per-XCD gfx clocks, MHz).  The matrix-core
+    peak scales with the clock, so the fraction of the peak at the observed clock is given beside
+    the spec one.  Null fields if the tool is missing or fails."""
+    import subprocess
+    import threading
+    res = {}
+
+    def sample():
+        time.sleep(0.6)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                               timeout=10)
+            res["json"] = r.stdout if r.returncode == 0 else None
+        except Exception:   # tool missing or hung: report nothing
+            res["json"] = None
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() or time.perf_counter() - t0 < 1.5:
+        for _ in range(10):
+            run_once()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 15.0:
+            break
+    th.join()
+    per_xcd = []
+    try:
+        clk = json.loads(res["json"])["gpu_data"][0]["clock"]
+        per_xcd = [float(v["clk"]["value"]) for k, v in sorted(clk.items()) if k.startswith("gfx_")]
+    except Exception:   # unexpected or missing output: report nothing
+        per_xcd = []
+    mean = sum(per_xcd) / len(per_xcd) if per_xcd else None
+    out = {"observed_gfx_mhz": round(mean, 1) if mean else None, "per_xcd_mhz": per_xcd, "spec_mhz": SPEC_MHZ,
+           "method": "amd-smi metric -c, read once during ~1.5 s of back-to-back searches of the same layer"}
+    if mean:
+        out["frac_of_peak_at_observed_clock"] = round(achieved / (PEAK_BF16_TFLOPS * mean / SPEC_MHZ), 4)
+        log(f"[bench] observed shader clock during the search {mean:.0f} MHz (spec {SPEC_MHZ}): "
+            f"{100 * achieved / (PEAK_BF16_TFLOPS * mean / SPEC_MHZ):.1f}% of the peak at that clock")
+    return out
 
 
 def bench_gemv_fused(A, I, torch, dev, iters):
