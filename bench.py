@@ -440,46 +440,50 @@ def _gemv_bytes(K, N, g=128):
 
 
 def observed_clock(run_once, torch, achieved):
-    """The shader clock the chip holds under the search: the search runs back to back for ~1.5 s and
-    `amd-smi metric -c` is read once in the middle of it (per-XCD gfx clocks, MHz).  The matrix-core
-    peak scales with the clock, so the fraction of the peak at the observed clock is given beside
-    the spec one.  Null fields if the tool is missing or fails."""
+    """The shader clock the chip holds under the search: the search runs back to back for ~3 s
+    while `amd-smi metric -c` is read five times from 1 s in (per-XCD gfx clocks, MHz; the SMU reports a short
+    average, so single readings scatter).  The matrix-core peak scales with the clock, so the
+    fraction of the peak at the median observed clock is given beside the spec one.  Null fields if
+    the tool is missing or fails."""
     import subprocess
     import threading
-    res = {}
+    samples = []
 
     def sample():
-        time.sleep(0.6)
-        try:
-            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
-                               timeout=10)
-            res["json"] = r.stdout if r.returncode == 0 else None
-        except Exception:   # tool missing or hung: report nothing
-            res["json"] = None
+        time.sleep(1.0)         # past the ramp from idle: earlier readings still average in the idle clock
+        for _ in range(5):
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                clk = json.loads(r.stdout)["gpu_data"][0]["clock"] if r.returncode == 0 else {}
+                per_xcd = [float(v["clk"]["value"]) for k, v in sorted(clk.items()) if k.startswith("gfx_")]
+                if per_xcd:
+                    samples.append(per_xcd)
+            except Exception:   # tool missing, hung or unexpected output: no sample
+                pass
+            time.sleep(0.3)
 
     th = threading.Thread(target=sample)
     th.start()
     t0 = time.perf_counter()
-    while th.is_alive() or time.perf_counter() - t0 < 1.5:
+    while th.is_alive():
         for _ in range(10):
             run_once()
         torch.cuda.synchronize()
-        if time.perf_counter() - t0 > 15.0:
+        if time.perf_counter() - t0 > 30.0:
             break
     th.join()
-    per_xcd = []
-    try:
-        clk = json.loads(res["json"])["gpu_data"][0]["clock"]
-        per_xcd = [float(v["clk"]["value"]) for k, v in sorted(clk.items()) if k.startswith("gfx_")]
-    except Exception:   # unexpected or missing output: report nothing
-        per_xcd = []
-    mean = sum(per_xcd) / len(per_xcd) if per_xcd else None
-    out = {"observed_gfx_mhz": round(mean, 1) if mean else None, "per_xcd_mhz": per_xcd, "spec_mhz": SPEC_MHZ,
-           "method": "amd-smi metric -c, read once during ~1.5 s of back-to-back searches of the same layer"}
-    if mean:
-        out["frac_of_peak_at_observed_clock"] = round(achieved / (PEAK_BF16_TFLOPS * mean / SPEC_MHZ), 4)
-        log(f"[bench] observed shader clock during the search {mean:.0f} MHz (spec {SPEC_MHZ}): "
-            f"{100 * achieved / (PEAK_BF16_TFLOPS * mean / SPEC_MHZ):.1f}% of the peak at that clock")
+    means = sorted(sum(x) / len(x) for x in samples)
+    med = means[len(means) // 2] if means else None
+    out = {"observed_gfx_mhz": round(med, 1) if med else None,
+           "samples_mhz": [round(m, 1) for m in means], "spec_mhz": SPEC_MHZ,
+           "method": "amd-smi metric -c, read five times from 1 s into ~3 s of back-to-back searches of "
+                     "the same layer; the median of the per-reading means over the 8 XCDs"}
+    if med:
+        out["frac_of_peak_at_observed_clock"] = round(achieved / (PEAK_BF16_TFLOPS * med / SPEC_MHZ), 4)
+        log(f"[bench] observed shader clock during the search {med:.0f} MHz (readings "
+            f"{', '.join(f'{m:.0f}' for m in means)}; spec {SPEC_MHZ}): "
+            f"{100 * achieved / (PEAK_BF16_TFLOPS * med / SPEC_MHZ):.1f}% of the peak at that clock")
     return out
 
 
