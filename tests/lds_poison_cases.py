@@ -150,11 +150,12 @@ def main():
         gpu = check_layer(L, g, zp, ng, label)
         T = L.X.shape[0]
         check_gemm(L, gpu, g, [1, 7, 16, 37, min(T, 256)], label)
-    # split-K products: M = 1 on 256- and 64-column workgroups, M = 16 and M = 40 with K split
+    # split-K products: M = 1 on 256- and 64-column workgroups, M = 16, 40 and 200 with K split
     check_packed_gemm(1, 8192, 1032, 128, True, seed=11)
     check_packed_gemm(1, 16384, 264, 128, True, seed=12)
     check_packed_gemm(16, 8192, 520, 128, True, seed=13)
     check_packed_gemm(40, 8192, 1032, 64, False, seed=14)
+    check_packed_gemm(200, 8192, 520, 128, True, seed=16)   # four 64-row tiles, K split
     check_clip(I.small(500, 256, 40, seed=15), 128, True, 11, 0.5, "g=128 asym 11 ratios")
     check_clip(I.small(300, 128, 24, seed=16, group_size=64, zero_point=False), 64, False, 7, 0.7, "g=64 sym 7 ratios")
     check_multi(420, 256, [64, 16, 24], 128, True, 17, "3 projections g=128")

@@ -42,6 +42,11 @@ SHAPES = [
     # 17..32 rows on 130 column tiles (K not split), 9 groups: wavefront 0 takes three (the odd
     # one after the two-group steps), the others two
     (24, 1152, 8320, 128, True),
+    # more than 64 rows: several 64-row tiles, ragged in rows (M % 64 != 0) and in columns
+    # (N % 256 == 8, 136 or 40), K split into blocks of an odd number of groups, each group size
+    (96, 4224, 264, 128, False),
+    (200, 2112, 136, 64, True),
+    (130, 1280, 8232, 32, True),
 ]
 
 _packed = {}
