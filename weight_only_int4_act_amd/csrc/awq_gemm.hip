@@ -10,6 +10,8 @@
 // x/s is rounded to bf16 once; each group's float32 partial is scaled by its Delta and added
 // to a float32 accumulator.  The 1/s* scaling is applied while the activation fragment is
 // formed, so no scaled copy of X is written.
+#include <algorithm>
+
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                                                    const float* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
                                                    uint16_t* __restrict__ Y, float* __restrict__ part,
-                                                   uint32_t* __restrict__ cnt) {
+                                                   uint32_t* __restrict__ cnt, int cstride) {
     constexpr int C = G / 32;
     __shared__ floatx4 red[3][MB][4][64];
     // the wavefront index in a scalar register: the group loop is then uniform per wavefront
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this workgroup's partial has landed
     const int tile = blockIdx.x + gridDim.x * blockIdx.y;
     uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt + (int64_t)tile * cstride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old != (uint32_t)(nz - 1)) return;
     constexpr int ZB = 4 / MB;   // K blocks whose loads are in flight together
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma(const u32x4* __restrict__ 
                 for (int i = 0; i < 4; ++i) tot[mb][i] += pv[u][mb][i];
     }
     write_y(tot);
-    if (lane == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(cnt + (int64_t)tile * cstride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Buffer resource over a byte range (accesses beyond it read zero) and a 16-byte-per-lane direct
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
                                                        const float* __restrict__ scales,
                                                        const uint8_t* __restrict__ zeros, int64_t K, int64_t N,
                                                        uint16_t* __restrict__ Y, float* __restrict__ part,
-                                                       uint32_t* __restrict__ cnt) {
+                                                       uint32_t* __restrict__ cnt, int cstride) {
     constexpr int C = G / 32, MB = 4;
     constexpr int NE = MB * C * 64;              // 16-byte x' entries of a group (MB row blocks x C chunks)
     constexpr int PT = NE / 256;                 // entries per thread (C of them)
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial has landed
     __syncthreads();
     const int tile = blockIdx.x + gridDim.x * blockIdx.y;
-    if (tid == 0) arrival = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) arrival = __hip_atomic_fetch_add(cnt + (int64_t)tile * cstride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrival != (uint32_t)(nz - 1)) return;
     floatx4 tot[MB][4];
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
             for (int i = 0; i < 4; ++i) tot[mb][i] += pv[mb][i];
     }
     write_y(tot);
-    if (tid == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(cnt + (int64_t)tile * cstride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                                                     const float* __restrict__ scales,
                                                     const uint8_t* __restrict__ zeros, int K, int N,
                                                     uint16_t* __restrict__ Y, float* __restrict__ part,
-                                                    uint32_t* __restrict__ cnt) {
+                                                    uint32_t* __restrict__ cnt, int cstride) {
     static_assert(G % VG == 0 && VG >= 32, "slice of a group");
     static_assert(QR == 1 || QR == 4, "lanes per column quadruple");
     constexpr int R = VG / 8;                    // code rows per slice
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     if (own) store4_agent(pr, (uint32_t)(((int64_t)kb * N + n0) * 4), v);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial has landed
     uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt + (int64_t)cb * cstride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old != (uint32_t)(nkb - 1)) return;
     // last arrival: the nkb partials of these columns in K-block order (loads of partials beyond
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
         for (int u = 0; u < 16; ++u) t += p[u];
     }
     if (own) *(uint2*)(Y + n0) = uint2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
-    if (lane == 0) __hip_atomic_store(cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(cnt + (int64_t)cb * cstride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 namespace {
@@ -757,12 +759,21 @@ hipError_t launch_mma(const uint16_t* X, int64_t M, const float* s, const uint32
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
     if (p.variant == 1)
-        k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
+        k_w4a16_mma<G, 1><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt, p.cstride);
     else if (p.variant == 2)
-        k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
+        k_w4a16_mma<G, 2><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt, p.cstride);
     else
-        k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt);
+        k_w4a16_mma_lds<G><<<grid, 256, 0, st>>>(Xp, Sg, p.mpad, M, codes, scales, zeros, K, N, Y, part, cnt, p.cstride);
     return hipGetLastError();
+}
+}  // namespace
+
+// Arrival counters of different output tiles sit on different 128-byte lines when the counter
+// region holds them that way, so that the atomics of different tiles are not serialized on one line.
+namespace {
+int counter_stride(int64_t n_counters) {
+    const int64_t words = (int64_t)(kGemmCounterBytes / sizeof(uint32_t));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(32, words / std::max<int64_t>(n_counters, 1)));
 }
 }  // namespace
 
@@ -797,6 +808,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
         }
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
+        p.cstride = counter_stride(p.grid_x);
         p.mpad = 1;
         p.off_cnt = 0;
         p.off_part = kGemmCounterBytes;
@@ -835,6 +847,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
         ks *= 2;
     p.grid_z = ks;
     p.ksplit = (int)ks;
+    p.cstride = counter_stride(tiles);
     p.off_cnt = 0;
     size_t off = kGemmCounterBytes;   // the counter region is never used for data
     p.off_part = off; off = align256(off + (ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0));
@@ -850,13 +863,13 @@ void launch_gemv(const uint16_t* X, const float* s, const uint32_t* codes, const
                  int64_t K, int64_t N, uint16_t* Y, float* part, uint32_t* cnt, const GemmPlan& p, hipStream_t st) {
     dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
     if (p.qr == 1 && p.gpw == 1)
-        k_w4a16_gemv<G, VG, 1, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+        k_w4a16_gemv<G, VG, 1, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt, p.cstride);
     else if (p.qr == 1)
-        k_w4a16_gemv<G, VG, 4, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+        k_w4a16_gemv<G, VG, 4, 1><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt, p.cstride);
     else if (p.gpw == 1)
-        k_w4a16_gemv<G, VG, 1, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+        k_w4a16_gemv<G, VG, 1, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt, p.cstride);
     else
-        k_w4a16_gemv<G, VG, 4, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt);
+        k_w4a16_gemv<G, VG, 4, 4><<<grid, 256, 0, st>>>(X, s, codes, scales, zeros, (int)K, (int)N, Y, part, cnt, p.cstride);
 }
 }  // namespace
 

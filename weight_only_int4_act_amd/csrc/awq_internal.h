@@ -98,6 +98,7 @@ struct GemmPlan {
                              // 2..16 rows: quantization groups of K per workgroup
     int gpw;                 // M = 1: slices per wavefront
     int qr;                  // M = 1: lanes per column quadruple (1: 256 columns per workgroup, 4: 64)
+    int cstride;             // arrival counter i at word i * cstride of the counter region
     // workspace layout (byte offsets): split-K partials, arrival counters (M <= 16, zero between
     // calls), x' in fragment order and group sums of x' (M > 16)
     size_t off_part, off_cnt, off_xp, off_sg, ws_bytes;
