@@ -798,13 +798,35 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int group_size) {
         p.gpw = (int)gpw;
         p.grid_y = (K / vg + kGemvWaves * gpw - 1) / (kGemvWaves * gpw);
         // several slices per wavefront (long K): 64 columns per workgroup instead of 256, four times
-        // as many workgroups with the same K split (measured on K = 28672: 32-33 against 35-36 us;
-        // on layers with one slice per wavefront it was no faster), while the column blocks'
-        // counters fit their region
+        // as many workgroups with the same K split (measured on K = 28672: 32-33 against 35-36 us),
+        // while the column blocks' counters fit their region.  Narrow layers (fewer than ~1536
+        // workgroups of 256 columns) also take 64 columns per workgroup, with the first of one slice
+        // of G rows, four slices of G/2 or four of G per wavefront that leaves at most 1280
+        // workgroups (on K = 8192: N = 1024 5.6 against 7.1 us, N = 8192 10.8 against 11.7 us,
+        // N = 10240 12.3 against 13.3 us); wide layers keep 256 columns
         p.qr = 1;
-        if (gpw > 1 && (N + 63) / 64 <= (int64_t)(kGemmCounterBytes / sizeof(uint32_t))) {
+        const int64_t blocks64 = (N + 63) / 64;
+        const bool fit64 = blocks64 <= (int64_t)(kGemmCounterBytes / sizeof(uint32_t));
+        if (gpw > 1 && fit64) {
             p.qr = 4;
-            p.grid_x = (N + 63) / 64;
+            p.grid_x = blocks64;
+        } else if (fit64 && p.grid_x * p.grid_y < 1536) {
+            const int64_t opts[3][2] = {{1, group_size}, {4, std::max(group_size / 2, 32)}, {4, group_size}};
+            gpw = 4;
+            vg = group_size;
+            for (const auto& o : opts) {
+                const int64_t kb = (K / o[1] + kGemvWaves * o[0] - 1) / (kGemvWaves * o[0]);
+                if (kb <= AWQ_GEMV_MAX_KSPLIT && blocks64 * kb <= 1280) {
+                    gpw = o[0];
+                    vg = o[1];
+                    break;
+                }
+            }
+            p.vgroup = (int)vg;
+            p.gpw = (int)gpw;
+            p.grid_y = (K / vg + kGemvWaves * gpw - 1) / (kGemvWaves * gpw);
+            p.qr = 4;
+            p.grid_x = blocks64;
         }
         p.grid_z = 1;
         p.ksplit = (int)p.grid_y;
