@@ -543,11 +543,11 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 }
 
 // ---------------------------------------------------------------- M = 1: decode-shaped GEMV
-// HBM-bound: every byte of packed weights is read once.  A workgroup owns 256 output columns and
-// 4*GPW slices of VG rows of K: wavefront w takes slices 4i + w, i < GPW.  Each lane reads 4
-// adjacent columns x 8 rows of codes with one 16-byte streaming load per code row (a wavefront
-// reads 1 KB of one code row: fully coalesced); the loads of the next slice are issued before the
-// current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values 128 + q with
+// HBM-bound: every byte of packed weights is read once.  A workgroup owns 256 output columns (64
+// on narrow layers and long K, see QR below) and 4*GPW slices of VG rows of K: wavefront w takes
+// slices 4i + w, i < GPW.  Each lane reads 4 adjacent columns x 8 rows of codes with one 16-byte
+// streaming load per code row (a wavefront reads 1 KB of code rows: whole 64- or 256-byte row
+// segments); the loads of the next slice are issued before the current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values 128 + q with
 // one shift and one and-or, and v_dot2c_f32_bf16 multiplies them with the pair (x'_k, x'_{k+4})
 // of activations x' = bf16(x/s) staged in LDS in that pair order.  The offset and the zero point
 // come out once per slice: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x', where sum x'
@@ -555,7 +555,8 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 // wavefront 0 through LDS and leave; wavefront 0 adds them in a fixed order.  With one K block it
 // writes Y.  Otherwise it writes the workgroup's float32 partial with agent-scope stores
 // (written through to the device-coherent level, not left in one die's L2), waits for them and
-// bumps the column block's arrival counter with one agent-scope atomic; the wavefront that
+// bumps the column block's arrival counter (on a 128-byte line of its own) with one agent-scope
+// atomic; the wavefront that
 // arrives last reads every partial of the block with agent-scope loads, adds them in K-block
 // order (so the result does not depend on the arrival order), writes Y and sets the counter back
 // to zero.  No wavefront waits on another workgroup, and there are no floating-point atomics.
@@ -571,8 +572,8 @@ constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 // and reads every code row of a slice.  QR = 4: the workgroup owns 64 columns; lane (r16, rq),
 // r16 = l % 16, rq = l / 16, owns columns 4 r16 .. 4 r16 + 3 and reads the code rows rq, rq + 4, ...
 // of a slice, and the four lanes of a column quadruple add their dot products with two lane swaps
-// at the end of the slice.  Narrow layers get four times as many workgroups without a longer K
-// split.
+// at the end of the slice.  Narrow layers and long K get four times as many workgroups without a
+// longer K split.
 template <int G, int VG, int kGemvGpw, int QR>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
                                                     const uint32_t* __restrict__ codes,
