@@ -548,8 +548,9 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 // slices 4i + w, i < GPW.  Each lane reads 4 adjacent columns x 8 rows of codes with one 16-byte
 // streaming load per code row (a wavefront reads 1 KB of code rows: whole 64- or 256-byte row
 // segments); the loads of the next slice are issued before the current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values 128 + q with
-// one shift and one and-or, and v_dot2c_f32_bf16 multiplies them with the pair (x'_k, x'_{k+4})
-// of activations x' = bf16(x/s) staged in LDS in that pair order.  The offset and the zero point
+// one shift and one and-or, multiplied with the pair (x'_k, x'_{k+4}) of activations x' = bf16(x/s)
+// staged in LDS in that pair order: by v_dot2c_f32_bf16 on 256-column workgroups, by the matrix
+// cores on 64-column ones (see QR below).  The offset and the zero point
 // come out once per slice: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x', where sum x'
 // adds the same bf16-rounded values the products used.  Wavefronts 1-3 hand their sums to
 // wavefront 0 through LDS and leave; wavefront 0 adds them in a fixed order.  With one K block it
@@ -571,8 +572,13 @@ constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 // QR: lanes per column quadruple.  QR = 1: lane l owns columns 4l .. 4l+3 of the workgroup's 256
 // and reads every code row of a slice.  QR = 4: the workgroup owns 64 columns; lane (r16, rq),
 // r16 = l % 16, rq = l / 16, owns columns 4 r16 .. 4 r16 + 3 and reads the code rows rq, rq + 4, ...
-// of a slice, and the four lanes of a column quadruple add their dot products with two lane swaps
-// at the end of the slice.  Narrow layers and long K get four times as many workgroups without a
+// of a slice.  That is the B-operand layout of a 16x16x32 bf16 matrix-core product: lane (r16, rq)
+// holds k slots 8 rq .. 8 rq + 7 of column r16, here code row rq (+4r) of column 4 r16 + c for the
+// c-th product.  Row 0 of the A operand carries x' of the same code rows (lanes r16 = 0), every
+// other row is zero, so row 0 of the result is the dot product over the four code rows for the 16
+// columns 4 r16 + c; one product per column of the quadruple replaces four v_dot2c per code word
+// and the lane swaps that would add the quadruple's four partial sums (about 7 instead of 11 VALU
+// instructions per code word).  Narrow layers and long K get four times as many workgroups without a
 // longer K split.
 template <int G, int VG, int kGemvGpw, int QR>
 __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ X, const float* __restrict__ s,
@@ -591,8 +597,10 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     __shared__ uint32_t xpair[NG][VG / 2];
     __shared__ float sxs[NG];
     __shared__ floatx4 red[kGemvWaves - 1][64];
+    __shared__ u32x4 zpad;   // QR = 4: the zero rows of the matrix-core A operand
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
+    if (QR == 4 && threadIdx.x == 0) zpad = u32x4{0u, 0u, 0u, 0u};   // read after the barrier below
     if constexpr (kLdsPoison) {   // debug build: x', its sums and the cross-wavefront sums start as NaN
         for (int i = threadIdx.x; i < NG * (VG / 2); i += 256) (&xpair[0][0])[i] = kLdsNan;
         if (threadIdx.x < NG) sxs[threadIdx.x] = __builtin_nanf("");
@@ -668,6 +676,29 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
         const int slot = kGemvWaves * i + wave;
         if (group_of(i) >= n_groups) return;
         float d[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (QR == 4) {
+            // one matrix-core product per column of the quadruple and group of four code rows; the
+            // operand pairs are formed in C so that the compiler inserts the VALU -> MFMA waits
+            floatx4 dm[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dm[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const bool row0 = (lane & 15) == 0;
+#pragma unroll
+            for (int r = 0; r < RL; ++r) {
+                const u32x4 a = *(row0 ? (const u32x4*)&xpair[slot][4 * (QR * r + rq)] : &zpad);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t w = b.cw[r][c];
+                    const u32x4 bo = u32x4{(w & nib) | bf128, ((w >> 4) & nib) | bf128, ((w >> 8) & nib) | bf128,
+                                           ((w >> 12) & nib) | bf128};
+                    dm[c] = mfma16x16x32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bo), dm[c]);
+                }
+            }
+            // row 0 of the result: lanes 0-15 (rq = 0), element 0; the other lanes hold zeros and
+            // write nothing
+#pragma unroll
+            for (int c = 0; c < 4; ++c) d[c] = dm[c][0];
+        } else
 #pragma unroll
         for (int r = 0; r < RL; ++r) {
             uint32_t xp[4];
@@ -682,14 +713,6 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
                     d[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
                                                            __builtin_bit_cast(bf16x2_t, xp[j]), d[c], false);
                 }
-            }
-        }
-        if constexpr (QR == 4) {
-            // the four lanes of the column quadruple (l, l ^ 16, l ^ 32, l ^ 48)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                d[c] += __shfl_xor(d[c], 16, 64);
-                d[c] += __shfl_xor(d[c], 32, 64);
             }
         }
         const float sx = sxs[slot];
@@ -714,7 +737,7 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     if (wave > 0) return;
     // wavefront 0, lane l: columns n0 .. n0 + 3 of the block
     const floatx4 v = ((floatx4{acc[0], acc[1], acc[2], acc[3]} + red[0][lane]) + red[1][lane]) + red[2][lane];
-    const bool own = nvalid && rq == 0;          // the other lanes of a quadruple hold the same sums
+    const bool own = nvalid && rq == 0;          // QR = 4: only lanes 0-15 hold the sums
     if (nkb == 1) {
         if (own) *(uint2*)(Y + n0) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         return;
