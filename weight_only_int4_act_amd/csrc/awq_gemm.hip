@@ -683,14 +683,18 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
 #pragma unroll
             for (int c = 0; c < 4; ++c) dm[c] = floatx4{0.f, 0.f, 0.f, 0.f};
             const bool row0 = (lane & 15) == 0;
+            // the mask in a vector register, so that each pair is one v_and_or_b32 (a VOP3 takes no
+            // literal; with the mask as a literal the compiler splits it into an and and an or)
+            uint32_t nibv;
+            asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(nibv));
 #pragma unroll
             for (int r = 0; r < RL; ++r) {
                 const u32x4 a = *(row0 ? (const u32x4*)&xpair[slot][4 * (QR * r + rq)] : &zpad);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const uint32_t w = b.cw[r][c];
-                    const u32x4 bo = u32x4{(w & nib) | bf128, ((w >> 4) & nib) | bf128, ((w >> 8) & nib) | bf128,
-                                           ((w >> 12) & nib) | bf128};
+                    const u32x4 bo = u32x4{(w & nibv) | bf128, ((w >> 4) & nibv) | bf128, ((w >> 8) & nibv) | bf128,
+                                           ((w >> 12) & nibv) | bf128};
                     dm[c] = mfma16x16x32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bo), dm[c]);
                 }
             }
