@@ -548,9 +548,9 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_mma_lds(const u32x4* __restric
 // slices 4i + w, i < GPW.  Each lane reads 4 adjacent columns x 8 rows of codes with one 16-byte
 // streaming load per code row (a wavefront reads 1 KB of code rows: whole 64- or 256-byte row
 // segments); the loads of the next slice are issued before the current one is consumed.  Nibbles k and k+4 of a code word become two bf16 values 128 + q with
-// one shift and one and-or, multiplied with the pair (x'_k, x'_{k+4}) of activations x' = bf16(x/s)
-// staged in LDS in that pair order: by v_dot2c_f32_bf16 on 256-column workgroups, by the matrix
-// cores on 64-column ones (see QR below).  The offset and the zero point
+// one shift and one and-or (the B operand of a 16x16x32 bf16 matrix-core product) and meet the pair
+// (x'_k, x'_{k+4}) of activations x' = bf16(x/s) staged in LDS in that pair order (in the A operand,
+// see QR below).  The offset and the zero point
 // come out once per slice: sum (q - z) x' = sum (128 + q) x' - (128 + z) sum x', where sum x'
 // adds the same bf16-rounded values the products used.  Wavefronts 1-3 hand their sums to
 // wavefront 0 through LDS and leave; wavefront 0 adds them in a fixed order.  With one K block it
@@ -570,7 +570,12 @@ constexpr int kGemvWaves = 4;    // wavefronts per workgroup
 // its own rows in the offset/zero correction, which is linear in the rows), so that more
 // workgroups share K and fill the GPU.
 // QR: lanes per column quadruple.  QR = 1: lane l owns columns 4l .. 4l+3 of the workgroup's 256
-// and reads every code row of a slice.  QR = 4: the workgroup owns 64 columns; lane (r16, rq),
+// and reads every code row of a slice.  One product per code row and column of the quadruple: lane
+// l = 16g + n supplies k slots 8g .. 8g + 7 of column n, i.e. its own column 4l + c, and row 4g of
+// the A operand carries x' of the code row in slot group g (lanes 0, 20, 40, 60; every other entry
+// is zero), so element 0 of lane l's result, row 4g and column n, is the dot product for its own
+// column: no lane exchange, about 7 VALU instructions per code word against 11 with four
+// v_dot2c_f32_bf16.  QR = 4: the workgroup owns 64 columns; lane (r16, rq),
 // r16 = l % 16, rq = l / 16, owns columns 4 r16 .. 4 r16 + 3 and reads the code rows rq, rq + 4, ...
 // of a slice.  That is the B-operand layout of a 16x16x32 bf16 matrix-core product: lane (r16, rq)
 // holds k slots 8 rq .. 8 rq + 7 of column r16, here code row rq (+4r) of column 4 r16 + c for the
@@ -597,10 +602,10 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
     __shared__ uint32_t xpair[NG][VG / 2];
     __shared__ float sxs[NG];
     __shared__ floatx4 red[kGemvWaves - 1][64];
-    __shared__ u32x4 zpad;   // QR = 4: the zero rows of the matrix-core A operand
+    __shared__ u32x4 zpad;   // the zero entries of the matrix-core A operand
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cb = blockIdx.x, kb = blockIdx.y, nkb = gridDim.y;
-    if (QR == 4 && threadIdx.x == 0) zpad = u32x4{0u, 0u, 0u, 0u};   // read after the barrier below
+    if (threadIdx.x == 0) zpad = u32x4{0u, 0u, 0u, 0u};   // read after the barrier below
     if constexpr (kLdsPoison) {   // debug build: x', its sums and the cross-wavefront sums start as NaN
         for (int i = threadIdx.x; i < NG * (VG / 2); i += 256) (&xpair[0][0])[i] = kLdsNan;
         if (threadIdx.x < NG) sxs[threadIdx.x] = __builtin_nanf("");
@@ -702,22 +707,29 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__
             // write nothing
 #pragma unroll
             for (int c = 0; c < 4; ++c) d[c] = dm[c][0];
-        } else
+        } else {
+            // QR = 1: lane l holds code row r of columns 4l + c; row 4g of A carries x' of that code
+            // row in k-slot group g (lanes 0, 20, 40, 60), so element 0 of lane l's result is the
+            // dot product for its own column 4l + c
+            floatx4 dm[4];
 #pragma unroll
-        for (int r = 0; r < RL; ++r) {
-            uint32_t xp[4];
+            for (int c = 0; c < 4; ++c) dm[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const bool diag = (lane & 15) == ((lane >> 4) << 2);
+            uint32_t nibv;
+            asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(nibv));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xp[j] = xpair[slot][4 * (QR * r + rq) + j];   // broadcast reads
+            for (int r = 0; r < RL; ++r) {
+                const u32x4 a = *(diag ? (const u32x4*)&xpair[slot][4 * r] : &zpad);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t w = b.cw[r][c];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t h = and_or(w >> (4 * j), nib, bf128);   // bf16 (128+q_j, 128+q_{j+4})
-                    d[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h),
-                                                           __builtin_bit_cast(bf16x2_t, xp[j]), d[c], false);
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t w = b.cw[r][c];
+                    const u32x4 bo = u32x4{(w & nibv) | bf128, ((w >> 4) & nibv) | bf128, ((w >> 8) & nibv) | bf128,
+                                           ((w >> 12) & nibv) | bf128};
+                    dm[c] = mfma16x16x32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bo), dm[c]);
                 }
             }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) d[c] = dm[c][0];
         }
         const float sx = sxs[slot];
 #pragma unroll
